@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark: one paged decode step of 4-bit, group-64 affine KV pages at head dim 256.
+
+A step is the whole hot path on one batch: quantize-on-append of the B*N new K/V rows into
+their pool slots, the split-K partial kernel over every cached token (block-table reads,
+dequantize-on-load, GQA-shared K/V rows, online softmax in f32), and the log-sum-exp merge.
+Inputs are seeded synthetic data resident in HBM before timing starts.
+
+Default workload ("c3"): 32 sequences with lengths drawn uniformly in [4096, 32768] tokens
+(sum 598,835), block size 32 with a shuffled block table, 16 query heads over 2 KV heads
+(GQA 8), head dim 256, one query row, K/V N(0,1) with 3 outlier channels per KV head
+scaled x8.
+
+Prints one JSON line (stdout, last line): effective K/V GB/s (bytes of codes + scales +
+biases of every cached token, per step) with the fraction of the 8 TB/s HBM peak,
+microseconds per step, the partial kernel's roofline figures, and the CPU oracle timed on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective KV GB/s (% of HBM peak) + µs per decode step, 4-bit paged D=256"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "device_common.hpp", "kernels.hpp"):
+        with open(os.path.join(ROOT, "decode_attention_paged_split_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, src_hash: str):
+    """HBM bytes per partial launch from the committed counter summary, if it was taken on the
+    current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", f"partial_kernel_pmc_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle's decode step on a bounded sample of sequences: append (quantize) the N new
+    rows, gather every cached row through the block table, unpack, dequantize in f64 and
+    run the f64 two-pass attention.  The sample grows until ~budget_s of CPU work."""
+    from oracle import attention, paged
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    order = list(range(w.B))
+    done, elapsed, eff = [], 0.0, 0
+    per = paged.quant.bytes_per_token_head(w.bits, w.D, w.group)
+    pool = paged.Pool(w.num_blocks, w.HK, w.BS, w.D, w.bits, w.group)
+    while order and elapsed < budget_s:
+        b = order.pop(0)
+        k, v = w.kv(b)
+        L = int(w.lengths[b])
+        pool.write(k[: L - w.N], v[: L - w.N], w.slots(b, 0, L - w.N))        # cached before the step
+        q = attention.q_f64(w.q_bits[b:b + 1])
+        t0 = time.perf_counter()
+        pool.write(k[L - w.N:], v[L - w.N:], w.slots(b, L - w.N, L))          # the step's new rows
+        kk, vv = pool.dequantized(w.table[b], L)
+        attention.decode_attention(q, [kk], [vv], w.lengths[b:b + 1], w.scale)
+        elapsed += time.perf_counter() - t0
+        done.append(b)
+        eff += L * w.HK * per
+    return {"value": eff / elapsed / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{len(done)} of {w.B} sequences ({sum(int(w.lengths[b]) for b in done)} tokens), "
+                      f"{elapsed:.1f} s of f64 NumPy: append-quantize of the new rows, gather, unpack, "
+                      f"dequantize, two-pass attention",
+            "seconds": round(elapsed, 2), "cpu": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--cold", action="store_true", help="write 1 GiB before each step (defeats the caches)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_paged_split_amd as kvq
+    from workloads import make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t_setup = time.time()
+    w = make_workload(args.workload)
+    log(f"[bench] workload {w.name}: B={w.B} HQ={w.HQ} HK={w.HK} D={w.D} N={w.N} bits={w.bits} "
+        f"BS={w.BS} sum(len)={int(w.lengths.sum())} NB={w.num_blocks}")
+    pool = kvq.Pool(w.num_blocks, w.HK, w.BS, w.D, w.bits, device=dev)
+    new_k, new_v, new_slots = [], [], []
+    for b in range(w.B):
+        k, v = w.kv(b)
+        L = int(w.lengths[b])
+        pool.append(torch.from_numpy(k[: L - w.N].view(np.int16)).to(dev),
+                    torch.from_numpy(v[: L - w.N].view(np.int16)).to(dev),
+                    torch.from_numpy(w.slots(b, 0, L - w.N)).to(dev))
+        new_k.append(k[L - w.N:]), new_v.append(v[L - w.N:]), new_slots.append(w.slots(b, L - w.N, L))
+        if b % 8 == 7:
+            log(f"[bench] filled {b + 1}/{w.B} sequences ({time.time() - t_setup:.0f} s)")
+    nk = torch.from_numpy(np.concatenate(new_k).view(np.int16)).to(dev)
+    nv = torch.from_numpy(np.concatenate(new_v).view(np.int16)).to(dev)
+    ns = torch.from_numpy(np.concatenate(new_slots)).to(dev)
+    q = torch.from_numpy(w.q_bits.view(np.int16)).to(dev)
+    table = torch.from_numpy(w.table).to(dev)
+    lengths = torch.from_numpy(w.lengths.astype(np.int32)).to(dev)
+    shape = kvq.make_shape(pool, w.B, w.HQ, w.N, w.max_blocks, w.max_len, args.partition_tokens, False)
+    ws = torch.empty(kvq.paged_decode_workspace_bytes(pool, shape), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.B, w.HQ, w.N, w.D), dtype=torch.bfloat16, device=dev)
+    pt = kvq.paged_decode_partition_tokens(pool, shape)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.time() - t_setup:.0f} s; partition {pt} tokens; workspace {ws.numel() >> 20} MiB")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        kvq.kv_append_quantize(pool, nk, nv, ns)
+        if ev is not None:
+            ev[1].record()
+        kvq.paged_decode_partial(q, pool, table, lengths, w.scale, shape, ws)
+        if ev is not None:
+            ev[2].record()
+        kvq.paged_decode_merge(pool, lengths, shape, ws, out)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        if flush is not None:
+            flush.fill_(1)
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(1)
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    app = [e[0].elapsed_time(e[1]) for e in evs]
+    par = [e[1].elapsed_time(e[2]) for e in evs]
+    mer = [e[2].elapsed_time(e[3]) for e in evs]
+    tot = [e[0].elapsed_time(e[3]) for e in evs]
+    ms_step = float(np.mean(tot)) if args.cold else evs[0][0].elapsed_time(evs[-1][3]) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (append {np.mean(app) * 1e3:.1f}, "
+        f"partial {np.mean(par) * 1e3:.1f}, merge {np.mean(mer) * 1e3:.1f}); wall {wall:.3f} s")
+
+    eff = w.effective_bytes()
+    gbs = eff / (ms_step * 1e-3) / 1e9
+    part_s = float(np.mean(par)) * 1e-3
+    achieved = eff / part_s / 1e9
+    src_hash = kernel_source_hash()
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles(w.name, src_hash),
+            "kernel": "partial_kernel", "kernel_us": round(part_s * 1e6, 2),
+            "algorithmic_bytes_per_launch": eff, "kernel_source_hash": src_hash}
+    rec = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: 4-bit affine g64 paged KV, B={w.B}, lengths U[4096,32768] "
+                               f"(sum {int(w.lengths.sum())}), BS={w.BS}, HQ={w.HQ}, HK={w.HK}, D={w.D}, "
+                               f"N={w.N}" if w.name == "c3" else w.name,
+                   "global_batch": w.B, "seq_len": w.max_len, "parallelism": "single GPU",
+                   "partition_tokens": pt, "cold": bool(args.cold)},
+        "us_per_step": round(ms_step * 1e3, 2), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "effective_bytes": eff,
+        "kernels_us": {"append": round(float(np.mean(app)) * 1e3, 2), "partial": round(part_s * 1e6, 2),
+                       "merge": round(float(np.mean(mer)) * 1e3, 2)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        log(f"[bench] oracle {rec['cpu_baseline']['value']:.3f} GB/s on {rec['cpu_baseline']['sample']}")
+    pool.close()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,284 @@
+"""Paged split-K decode attention over bf16 / affine-quantized KV pages, for MI355X (gfx950).
+
+A thin ctypes binding over ``libkvq.so`` (the C ABI in ``include/kvq.h``).  Every step of
+the path runs in the library's HIP kernels; this module only marshals arguments.  PyTorch
+supplies device memory (``torch.empty`` / ``torch.zeros`` on a ROCm device) and the
+current stream.  There is no CPU fallback: importing works without a GPU, but every
+compute call needs the built library and a GPU, and raises otherwise.
+
+Functions with the C ABI's names:
+
+* ``kv_pool_create(desc)`` / ``kv_pool_wrap(desc, planes)`` / ``kv_pool_destroy(handle)``
+* ``kv_append_quantize(pool, k, v, slots)``
+* ``paged_decode_workspace_bytes(pool, shape)``
+* ``paged_decode_attention(q, pool, block_table, lengths, scale, shape, workspace, out)``
+* ``kv_gather_debug(pool, block_table, lengths, batch, max_blocks, max_len, out_planes)``
+
+plus ``Pool`` (planes held as torch tensors, wrapped by the library) and ``decode``
+(allocates workspace and output, then calls ``paged_decode_attention``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+__all__ = [
+    "KvqError", "PoolDesc", "DecodeShape", "Pool", "decode", "lib", "kv_pool_create", "kv_pool_wrap",
+    "kv_pool_destroy", "kv_pool_plane_bytes", "kv_append_quantize", "paged_decode_workspace_bytes",
+    "paged_decode_partition_tokens", "paged_decode_attention", "paged_decode_partial",
+    "paged_decode_merge", "kv_gather_debug", "make_shape", "gather", "PLANES", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+
+PLANE_K, PLANE_V, PLANE_K_SCALE, PLANE_K_BIAS, PLANE_V_SCALE, PLANE_V_BIAS = range(6)
+PLANES = ("k", "v", "k_scale", "k_bias", "v_scale", "v_bias")
+STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID", -2: "KVQ_ERR_UNSUPPORTED", -3: "KVQ_ERR_OOM",
+          -4: "KVQ_ERR_HIP", -5: "KVQ_ERR_WORKSPACE", -6: "KVQ_ERR_RANGE"}
+
+
+class KvqError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("bits", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+
+
+class DecodeShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("q_rows", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("max_len", ctypes.c_int32),
+                ("partition_tokens", ctypes.c_int32), ("out_f32", ctypes.c_int32)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+_P = ctypes.c_void_p
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m decode_attention_paged_split_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "kvq_last_error": (ctypes.c_char_p, []),
+            "kvq_version": (ctypes.c_char_p, []),
+            "kv_pool_plane_bytes": (ctypes.c_size_t, [ctypes.POINTER(PoolDesc), ctypes.c_int32]),
+            "kv_pool_create": (ctypes.c_int, [ctypes.POINTER(PoolDesc), _PP]),
+            "kv_pool_wrap": (ctypes.c_int, [ctypes.POINTER(PoolDesc), _P * 6, _PP]),
+            "kv_pool_destroy": (ctypes.c_int, [_P]),
+            "kv_pool_plane": (ctypes.c_int, [_P, ctypes.c_int32, _PP, ctypes.POINTER(ctypes.c_size_t)]),
+            "kv_pool_describe": (ctypes.c_int, [_P, ctypes.POINTER(PoolDesc)]),
+            "kv_append_quantize": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P]),
+            "paged_decode_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.POINTER(DecodeShape)]),
+            "paged_decode_partition_tokens": (ctypes.c_int32, [_P, ctypes.POINTER(DecodeShape)]),
+            "paged_decode_attention": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_float,
+                                                      ctypes.POINTER(DecodeShape), _P, ctypes.c_size_t,
+                                                      _P, _P]),
+            "paged_decode_partial": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_float, ctypes.POINTER(DecodeShape),
+                                                    _P, ctypes.c_size_t, _P]),
+            "paged_decode_merge": (ctypes.c_int, [_P, _P, ctypes.POINTER(DecodeShape), _P, ctypes.c_size_t,
+                                                  _P, _P]),
+            "kv_gather_debug": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               _P * 6, _P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        raise KvqError(code, lib().kvq_last_error().decode())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need_cuda(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("kvq kernels take device tensors; got a CPU tensor")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("kvq kernels take contiguous tensors")
+
+
+# ------------------------------------------------------------------ C ABI, same names
+
+def kv_pool_plane_bytes(desc: PoolDesc, plane: int) -> int:
+    return int(lib().kv_pool_plane_bytes(ctypes.byref(desc), plane))
+
+
+def kv_pool_create(desc: PoolDesc) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(lib().kv_pool_create(ctypes.byref(desc), ctypes.byref(h)))
+    return h
+
+
+def kv_pool_wrap(desc: PoolDesc, planes: Sequence[int]) -> ctypes.c_void_p:
+    arr = (_P * 6)(*[ctypes.c_void_p(p) for p in planes])
+    h = ctypes.c_void_p()
+    _check(lib().kv_pool_wrap(ctypes.byref(desc), arr, ctypes.byref(h)))
+    return h
+
+
+def kv_pool_destroy(handle) -> None:
+    _check(lib().kv_pool_destroy(handle))
+
+
+def kv_append_quantize(pool: "Pool", k, v, slots, stream=None) -> None:
+    _need_cuda(k, v, slots)
+    T = int(slots.shape[0])
+    _check(lib().kv_append_quantize(pool.handle, _ptr(k), _ptr(v), _ptr(slots), T, _stream(stream)))
+
+
+def paged_decode_workspace_bytes(pool: "Pool", shape: DecodeShape) -> int:
+    n = int(lib().paged_decode_workspace_bytes(pool.handle, ctypes.byref(shape)))
+    if n == 0:
+        raise KvqError(-1, lib().kvq_last_error().decode())
+    return n
+
+
+def paged_decode_partition_tokens(pool: "Pool", shape: DecodeShape) -> int:
+    return int(lib().paged_decode_partition_tokens(pool.handle, ctypes.byref(shape)))
+
+
+def paged_decode_attention(q, pool: "Pool", block_table, lengths, scale: float, shape: DecodeShape,
+                           workspace, out, stream=None) -> None:
+    _need_cuda(q, block_table, lengths, workspace, out)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().paged_decode_attention(_ptr(q), pool.handle, _ptr(block_table), _ptr(lengths),
+                                        float(scale), ctypes.byref(shape), _ptr(workspace), ws_bytes,
+                                        _ptr(out), _stream(stream)))
+
+
+def paged_decode_partial(q, pool: "Pool", block_table, lengths, scale: float, shape: DecodeShape,
+                         workspace, stream=None) -> None:
+    _need_cuda(q, block_table, lengths, workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().paged_decode_partial(_ptr(q), pool.handle, _ptr(block_table), _ptr(lengths), float(scale),
+                                      ctypes.byref(shape), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def paged_decode_merge(pool: "Pool", lengths, shape: DecodeShape, workspace, out, stream=None) -> None:
+    _need_cuda(lengths, workspace, out)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().paged_decode_merge(pool.handle, _ptr(lengths), ctypes.byref(shape), _ptr(workspace), ws_bytes,
+                                    _ptr(out), _stream(stream)))
+
+
+def kv_gather_debug(pool: "Pool", block_table, lengths, batch: int, max_blocks: int, max_len: int,
+                    out_planes: Sequence, stream=None) -> None:
+    _need_cuda(block_table, lengths, *[o for o in out_planes if o is not None])
+    arr = (_P * 6)(*[_ptr(o) if o is not None else ctypes.c_void_p(0) for o in out_planes])
+    _check(lib().kv_gather_debug(pool.handle, _ptr(block_table), _ptr(lengths), batch, max_blocks,
+                                 max_len, arr, _stream(stream)))
+
+
+# ------------------------------------------------------------------ convenience
+
+class Pool:
+    """A block pool whose planes are torch device tensors wrapped by the library.
+
+    planes["k"], planes["v"]: uint32 codes [NB, HK, BS, D*bits/32] (affine) or bf16 bit
+    patterns as int16 [NB, HK, BS, D] (bits == 16); planes["{k,v}_{scale,bias}"]: bf16
+    bit patterns as int16 [NB, HK, BS, D/64].
+    """
+
+    def __init__(self, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
+                 bits: int, group_size: int = 64, device=None):
+        import torch
+        self.desc = PoolDesc(num_blocks, num_kv_heads, block_size, head_dim, bits, group_size)
+        dev = torch.device(device) if device is not None else torch.device("cuda")
+        shape = lambda w: (num_blocks, num_kv_heads, block_size, w)  # noqa: E731
+        if bits == 16:
+            self.planes = {"k": torch.zeros(shape(head_dim), dtype=torch.int16, device=dev),
+                           "v": torch.zeros(shape(head_dim), dtype=torch.int16, device=dev)}
+        else:
+            W, G = head_dim * bits // 32, head_dim // group_size
+            # uint32 codes held as int32 storage (torch has no uint32 arithmetic on every backend)
+            self.planes = {"k": torch.zeros(shape(W), dtype=torch.int32, device=dev),
+                           "v": torch.zeros(shape(W), dtype=torch.int32, device=dev)}
+            for n in PLANES[2:]:
+                self.planes[n] = torch.zeros(shape(G), dtype=torch.int16, device=dev)
+        ptrs = [self.planes[n].data_ptr() if n in self.planes else 0 for n in PLANES]
+        for i, n in enumerate(PLANES):
+            if n in self.planes:
+                want = kv_pool_plane_bytes(self.desc, i)
+                t = self.planes[n]
+                assert t.numel() * t.element_size() == want, (n, want)
+        self.handle = kv_pool_wrap(self.desc, ptrs)
+
+    @property
+    def bits(self) -> int:
+        return self.desc.bits
+
+    def append(self, k, v, slots, stream=None) -> None:
+        kv_append_quantize(self, k, v, slots, stream)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            kv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def make_shape(pool: Pool, batch: int, num_q_heads: int, q_rows: int, max_blocks: int, max_len: int,
+               partition_tokens: int = 0, out_f32: bool = False) -> DecodeShape:
+    return DecodeShape(batch, num_q_heads, q_rows, max_blocks, max_len, partition_tokens, int(out_f32))
+
+
+def decode(q, pool: Pool, block_table, lengths, scale: float, max_len: int, partition_tokens: int = 0,
+           out_f32: bool = False, workspace=None, out=None, stream=None):
+    """Allocate (if not given) workspace and output, then run paged_decode_attention.
+
+    q: bf16 [B, HQ, N, D] (torch.bfloat16 or int16 bit patterns); block_table int32 [B, M];
+    lengths int32 [B].  Returns out [B, HQ, N, D] (bfloat16, or float32 if out_f32).
+    """
+    import torch
+    B, HQ, N, D = q.shape
+    shape = make_shape(pool, B, HQ, N, block_table.shape[1], max_len, partition_tokens, out_f32)
+    if workspace is None:
+        workspace = torch.empty(paged_decode_workspace_bytes(pool, shape), dtype=torch.uint8,
+                                device=q.device)
+    if out is None:
+        out = torch.empty((B, HQ, N, D), dtype=torch.float32 if out_f32 else torch.bfloat16,
+                          device=q.device)
+    paged_decode_attention(q, pool, block_table, lengths, scale, shape, workspace, out, stream)
+    return out
+
+
+def gather(pool: Pool, block_table, lengths, max_len: int, stream=None) -> Dict[str, object]:
+    """kv_gather_debug into fresh tensors: {plane: [B, HK, max_len, width]}."""
+    import torch
+    B, M = block_table.shape
+    outs = {}
+    for n, t in pool.planes.items():
+        outs[n] = torch.empty((B, pool.desc.num_kv_heads, max_len, t.shape[-1]), dtype=t.dtype,
+                              device=t.device)
+    kv_gather_debug(pool, block_table, lengths, B, M, max_len, [outs.get(n) for n in PLANES], stream)
+    return outs

@@ -1,0 +1,380 @@
+// kvq C ABI: argument validation, pool management, launch configuration.
+// Declarations and the contract of every entry point are in include/kvq.h.
+#include "../../include/kvq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "kernels.hpp"
+
+struct kvq_pool {
+  kvq_pool_desc desc;
+  void* planes[KVQ_NUM_PLANES];
+  size_t bytes[KVQ_NUM_PLANES];
+  bool owned;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int plane_count(int bits) { return bits == 16 ? 2 : 6; }
+
+int validate_desc(const kvq_pool_desc* d) {
+  if (!d) return fail(KVQ_ERR_INVALID, "pool descriptor is NULL");
+  if (d->num_blocks < 1 || d->num_kv_heads < 1 || d->block_size < 1 || d->head_dim < 1)
+    return fail(KVQ_ERR_INVALID, "pool sizes must be positive (NB=%d HK=%d BS=%d D=%d)",
+                d->num_blocks, d->num_kv_heads, d->block_size, d->head_dim);
+  if (!(d->bits == 16 || d->bits == 8 || d->bits == 4 || d->bits == 2))
+    return fail(KVQ_ERR_UNSUPPORTED, "bits must be 16 (bf16 pages) or 8, 4, 2 (affine), got %d", d->bits);
+  if (d->group_size != 64)
+    return fail(KVQ_ERR_UNSUPPORTED, "group_size must be 64, got %d", d->group_size);
+  if (d->head_dim % 64 != 0 || d->head_dim > 256)
+    return fail(KVQ_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256, got %d", d->head_dim);
+  const size_t rows = (size_t)d->num_blocks * d->num_kv_heads * d->block_size;
+  if (rows > (size_t)1 << 40) return fail(KVQ_ERR_INVALID, "pool too large");
+  return KVQ_OK;
+}
+
+size_t plane_row_bytes(const kvq_pool_desc* d, int plane) {
+  if (d->bits == 16) return (plane <= KVQ_PLANE_V) ? (size_t)d->head_dim * 2 : 0;
+  if (plane <= KVQ_PLANE_V) return (size_t)d->head_dim * d->bits / 8;
+  if (plane < KVQ_NUM_PLANES) return (size_t)(d->head_dim / d->group_size) * 2;
+  return 0;
+}
+
+int device_cus() {
+  static int cus = 0;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  });
+  return cus;
+}
+
+constexpr int MAX_PARTS = 8192;
+
+int qvw_for(int qv) {
+  for (int w = 8; w >= 1; w /= 2)
+    if (qv % w == 0) return w;
+  return 1;
+}
+
+// Tokens per split-K partition: the smallest power of two >= 64 for which the upper bound
+// on workgroups (every sequence at max_len) stays within 8 per compute unit, so that the
+// grid fills the chip while partial traffic stays small.  KVQ_PARTITION_TOKENS overrides.
+int choose_partition(const kvq_pool* pool, const kvq_decode_shape* s) {
+  if (s->partition_tokens > 0) return s->partition_tokens;
+  if (const char* e = std::getenv("KVQ_PARTITION_TOKENS")) {
+    const int v = std::atoi(e);
+    if (v > 0) return v;
+  }
+  const int hk = pool->desc.num_kv_heads;
+  const int qv = (s->num_q_heads / hk) * s->q_rows;
+  const int qg = qv / qvw_for(qv);
+  const long budget = 8L * device_cus();
+  int pt = 64;
+  while (pt < (1 << 20)) {
+    const long parts = (s->max_len + pt - 1) / pt;
+    if ((long)s->batch * hk * qg * parts <= budget && parts <= MAX_PARTS) break;
+    pt *= 2;
+  }
+  return pt;
+}
+
+int validate_shape(const kvq_pool* pool, const kvq_decode_shape* s) {
+  if (!pool) return fail(KVQ_ERR_INVALID, "pool is NULL");
+  if (!s) return fail(KVQ_ERR_INVALID, "decode shape is NULL");
+  if (s->batch < 1 || s->num_q_heads < 1 || s->max_blocks_per_seq < 1 || s->max_len < 1)
+    return fail(KVQ_ERR_INVALID, "batch, num_q_heads, max_blocks_per_seq and max_len must be positive");
+  if (s->q_rows < 1 || s->q_rows > 8)
+    return fail(KVQ_ERR_UNSUPPORTED, "q_rows must be 1..8 for the direct paged read, got %d", s->q_rows);
+  if (s->num_q_heads % pool->desc.num_kv_heads != 0)
+    return fail(KVQ_ERR_UNSUPPORTED, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                s->num_q_heads, pool->desc.num_kv_heads);
+  if (s->q_rows > s->max_len) return fail(KVQ_ERR_INVALID, "q_rows exceeds max_len");
+  if (s->batch > 65535 || (long)pool->desc.num_kv_heads * s->num_q_heads > 65535)
+    return fail(KVQ_ERR_UNSUPPORTED, "batch and num_q_heads * num_kv_heads must stay below 65536");
+  if ((long)s->max_blocks_per_seq * pool->desc.block_size < s->max_len)
+    return fail(KVQ_ERR_RANGE, "max_len %d exceeds the block table's capacity %ld tokens", s->max_len,
+                (long)s->max_blocks_per_seq * pool->desc.block_size);
+  if (s->partition_tokens < 0) return fail(KVQ_ERR_INVALID, "partition_tokens must be >= 0");
+  const int pt = choose_partition(pool, s);
+  if ((s->max_len + pt - 1) / pt > MAX_PARTS)
+    return fail(KVQ_ERR_UNSUPPORTED, "more than %d partitions (max_len %d, partition %d)", MAX_PARTS,
+                s->max_len, pt);
+  const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
+  if (!kvq::partial_supported(pool->desc.bits, pool->desc.head_dim, qvw_for(qv)))
+    return fail(KVQ_ERR_UNSUPPORTED, "no kernel for bits=%d D=%d", pool->desc.bits, pool->desc.head_dim);
+  return KVQ_OK;
+}
+
+size_t workspace_layout(const kvq_pool* pool, const kvq_decode_shape* s, int pt, size_t* ml_off) {
+  const size_t parts = (size_t)(s->max_len + pt - 1) / pt;
+  const size_t rows = (size_t)s->batch * s->num_q_heads * s->q_rows;
+  size_t o_bytes = rows * parts * pool->desc.head_dim * sizeof(float);
+  o_bytes = (o_bytes + 255) & ~(size_t)255;
+  *ml_off = o_bytes;
+  return o_bytes + rows * parts * 2 * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_last_error(void) { return g_err.c_str(); }
+
+const char* kvq_version(void) { return "kvq 0.1 (gfx950)"; }
+
+size_t kv_pool_plane_bytes(const kvq_pool_desc* desc, int32_t plane) {
+  if (!desc || plane < 0 || plane >= KVQ_NUM_PLANES) return 0;
+  if (validate_desc(desc) != KVQ_OK) return 0;
+  return plane_row_bytes(desc, plane) * desc->num_blocks * desc->num_kv_heads * desc->block_size;
+}
+
+int kv_pool_create(const kvq_pool_desc* desc, kvq_pool** out) {
+  if (!out) return fail(KVQ_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (int r = validate_desc(desc)) return r;
+  kvq_pool* p = new kvq_pool();
+  p->desc = *desc;
+  p->owned = true;
+  for (int i = 0; i < KVQ_NUM_PLANES; ++i) {
+    p->planes[i] = nullptr;
+    p->bytes[i] = kv_pool_plane_bytes(desc, i);
+    if (p->bytes[i] == 0) continue;
+    hipError_t e = hipMalloc(&p->planes[i], p->bytes[i]);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      kv_pool_destroy(p);
+      return fail(KVQ_ERR_OOM, "hipMalloc of %zu bytes for plane %d failed: %s", p->bytes[i], i,
+                  hipGetErrorString(e));
+    }
+    e = hipMemset(p->planes[i], 0, p->bytes[i]);
+    if (e != hipSuccess) {
+      kv_pool_destroy(p);
+      return hip_fail(e, "hipMemset");
+    }
+  }
+  *out = p;
+  return KVQ_OK;
+}
+
+int kv_pool_wrap(const kvq_pool_desc* desc, void* const planes[KVQ_NUM_PLANES], kvq_pool** out) {
+  if (!out) return fail(KVQ_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (int r = validate_desc(desc)) return r;
+  if (!planes) return fail(KVQ_ERR_INVALID, "planes is NULL");
+  kvq_pool* p = new kvq_pool();
+  p->desc = *desc;
+  p->owned = false;
+  for (int i = 0; i < KVQ_NUM_PLANES; ++i) {
+    p->bytes[i] = kv_pool_plane_bytes(desc, i);
+    p->planes[i] = p->bytes[i] ? planes[i] : nullptr;
+    if (p->bytes[i] && (!planes[i] || !aligned(planes[i], 16))) {
+      delete p;
+      return fail(KVQ_ERR_INVALID, "plane %d is NULL or not 16-byte aligned", i);
+    }
+  }
+  *out = p;
+  return KVQ_OK;
+}
+
+int kv_pool_destroy(kvq_pool* pool) {
+  if (!pool) return KVQ_OK;
+  if (pool->owned)
+    for (int i = 0; i < KVQ_NUM_PLANES; ++i)
+      if (pool->planes[i]) (void)hipFree(pool->planes[i]);
+  delete pool;
+  return KVQ_OK;
+}
+
+int kv_pool_plane(const kvq_pool* pool, int32_t plane, void** dev_ptr, size_t* bytes) {
+  if (!pool || !dev_ptr || !bytes) return fail(KVQ_ERR_INVALID, "NULL argument");
+  if (plane < 0 || plane >= KVQ_NUM_PLANES || pool->bytes[plane] == 0)
+    return fail(KVQ_ERR_INVALID, "pool has no plane %d", plane);
+  *dev_ptr = pool->planes[plane];
+  *bytes = pool->bytes[plane];
+  return KVQ_OK;
+}
+
+int kv_pool_describe(const kvq_pool* pool, kvq_pool_desc* out) {
+  if (!pool || !out) return fail(KVQ_ERR_INVALID, "NULL argument");
+  *out = pool->desc;
+  return KVQ_OK;
+}
+
+int kv_append_quantize(kvq_pool* pool, const uint16_t* k, const uint16_t* v, const int64_t* slots,
+                       int32_t num_tokens, void* stream) {
+  if (!pool) return fail(KVQ_ERR_INVALID, "pool is NULL");
+  if (num_tokens < 0) return fail(KVQ_ERR_INVALID, "num_tokens < 0");
+  if (num_tokens == 0) return KVQ_OK;
+  if (!k || !v || !slots) return fail(KVQ_ERR_INVALID, "k, v and slots must be device pointers");
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slots, 8))
+    return fail(KVQ_ERR_INVALID, "k and v must be 16-byte aligned, slots 8-byte aligned");
+  const kvq_pool_desc& d = pool->desc;
+  kvq::AppendArgs a{};
+  a.k = k; a.v = v; a.slots = slots;
+  a.k_plane = pool->planes[KVQ_PLANE_K]; a.v_plane = pool->planes[KVQ_PLANE_V];
+  a.k_scale = pool->planes[KVQ_PLANE_K_SCALE]; a.k_bias = pool->planes[KVQ_PLANE_K_BIAS];
+  a.v_scale = pool->planes[KVQ_PLANE_V_SCALE]; a.v_bias = pool->planes[KVQ_PLANE_V_BIAS];
+  a.T = num_tokens; a.HK = d.num_kv_heads; a.D = d.head_dim; a.BS = d.block_size;
+  a.num_slots = (int64_t)d.num_blocks * d.block_size;
+  hipError_t e = kvq::launch_append(a, d.bits, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return KVQ_OK;
+}
+
+size_t paged_decode_workspace_bytes(const kvq_pool* pool, const kvq_decode_shape* shape) {
+  if (validate_shape(pool, shape) != KVQ_OK) return 0;
+  size_t ml_off = 0;
+  return workspace_layout(pool, shape, choose_partition(pool, shape), &ml_off);
+}
+
+int32_t paged_decode_partition_tokens(const kvq_pool* pool, const kvq_decode_shape* shape) {
+  if (validate_shape(pool, shape) != KVQ_OK) return 0;
+  return choose_partition(pool, shape);
+}
+
+namespace {
+
+struct Plan {
+  kvq::PartialArgs a;
+  kvq::MergeArgs m;
+  int qvw;
+};
+
+int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, const int32_t* lengths, float scale,
+         const kvq_decode_shape* shape, void* workspace, size_t workspace_bytes, void* out, bool need_q,
+         bool need_out, Plan* P) {
+  if (int r = validate_shape(pool, shape)) return r;
+  if ((need_q && (!q || !block_table)) || !lengths || !workspace || (need_out && !out))
+    return fail(KVQ_ERR_INVALID, "q, block_table, lengths, workspace and out must be device pointers");
+  if ((need_q && (!aligned(q, 16) || !aligned(block_table, 4))) || !aligned(lengths, 4) ||
+      !aligned(workspace, 16) || (need_out && !aligned(out, shape->out_f32 ? 4 : 2)))
+    return fail(KVQ_ERR_INVALID, "misaligned pointer (q and workspace need 16 bytes)");
+  const int pt = choose_partition(pool, shape);
+  size_t ml_off = 0;
+  const size_t need = workspace_layout(pool, shape, pt, &ml_off);
+  if (workspace_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  const kvq_pool_desc& d = pool->desc;
+  const int parts = (shape->max_len + pt - 1) / pt;
+  const int qv = (shape->num_q_heads / d.num_kv_heads) * shape->q_rows;
+  P->qvw = qvw_for(qv);
+
+  kvq::PartialArgs& a = P->a;
+  a = kvq::PartialArgs{};
+  a.q = q;
+  a.k = pool->planes[KVQ_PLANE_K]; a.v = pool->planes[KVQ_PLANE_V];
+  a.ks = static_cast<const uint16_t*>(pool->planes[KVQ_PLANE_K_SCALE]);
+  a.kb = static_cast<const uint16_t*>(pool->planes[KVQ_PLANE_K_BIAS]);
+  a.vs = static_cast<const uint16_t*>(pool->planes[KVQ_PLANE_V_SCALE]);
+  a.vb = static_cast<const uint16_t*>(pool->planes[KVQ_PLANE_V_BIAS]);
+  a.table = block_table; a.lengths = lengths;
+  a.opart = static_cast<float*>(workspace);
+  a.ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_off);
+  a.scale_log2e = scale * 1.4426950408889634f;
+  a.HQ = shape->num_q_heads; a.HK = d.num_kv_heads; a.N = shape->q_rows; a.BS = d.block_size;
+  a.bs_shift = -1;
+  for (int s = 0; s < 31; ++s)
+    if ((1 << s) == d.block_size) a.bs_shift = s;
+  a.max_blocks = shape->max_blocks_per_seq; a.num_blocks = d.num_blocks; a.max_len = shape->max_len;
+  a.part_tokens = pt; a.num_parts = parts; a.qgroups = qv / P->qvw;
+
+  kvq::MergeArgs& m = P->m;
+  m = kvq::MergeArgs{};
+  m.opart = a.opart; m.ml = a.ml; m.lengths = lengths; m.out = out;
+  m.HQ = shape->num_q_heads; m.N = shape->q_rows; m.D = d.head_dim; m.part_tokens = pt;
+  m.num_parts = parts; m.out_f32 = shape->out_f32 ? 1 : 0; m.max_len = shape->max_len;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+int paged_decode_partial(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table,
+                         const int32_t* lengths, float scale, const kvq_decode_shape* shape, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Plan P;
+  if (int r = plan(q, pool, block_table, lengths, scale, shape, workspace, workspace_bytes, nullptr, true, false, &P))
+    return r;
+  hipError_t e = kvq::launch_partial(P.a, pool->desc.bits, pool->desc.head_dim, P.qvw, shape->batch,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "partial launch");
+  return KVQ_OK;
+}
+
+int paged_decode_merge(const kvq_pool* pool, const int32_t* lengths, const kvq_decode_shape* shape,
+                       const void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  Plan P;
+  if (int r = plan(nullptr, pool, nullptr, lengths, 0.0f, shape, const_cast<void*>(workspace), workspace_bytes, out,
+                   false, true, &P))
+    return r;
+  hipError_t e = kvq::launch_merge(P.m, shape->batch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return KVQ_OK;
+}
+
+int paged_decode_attention(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table,
+                           const int32_t* lengths, float scale, const kvq_decode_shape* shape,
+                           void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  Plan P;
+  if (int r = plan(q, pool, block_table, lengths, scale, shape, workspace, workspace_bytes, out, true, true, &P))
+    return r;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = kvq::launch_partial(P.a, pool->desc.bits, pool->desc.head_dim, P.qvw, shape->batch, st);
+  if (e != hipSuccess) return hip_fail(e, "partial launch");
+  e = kvq::launch_merge(P.m, shape->batch, st);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return KVQ_OK;
+}
+
+int kv_gather_debug(const kvq_pool* pool, const int32_t* block_table, const int32_t* lengths, int32_t batch,
+                    int32_t max_blocks_per_seq, int32_t max_len, void* const out_planes[KVQ_NUM_PLANES],
+                    void* stream) {
+  if (!pool || !block_table || !lengths || !out_planes) return fail(KVQ_ERR_INVALID, "NULL argument");
+  if (batch < 1 || max_blocks_per_seq < 1 || max_len < 1) return fail(KVQ_ERR_INVALID, "sizes must be positive");
+  const kvq_pool_desc& d = pool->desc;
+  for (int p = 0; p < plane_count(d.bits); ++p) {
+    if (!out_planes[p]) return fail(KVQ_ERR_INVALID, "out plane %d is NULL", p);
+    kvq::GatherArgs g{};
+    g.plane = static_cast<const uint8_t*>(pool->planes[p]);
+    g.out = static_cast<uint8_t*>(out_planes[p]);
+    g.table = block_table; g.lengths = lengths;
+    g.B = batch; g.HK = d.num_kv_heads; g.BS = d.block_size; g.max_blocks = max_blocks_per_seq;
+    g.max_len = max_len; g.num_blocks = d.num_blocks;
+    g.row_bytes = (int)plane_row_bytes(&d, p);
+    hipError_t e = kvq::launch_gather(g, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "gather launch");
+  }
+  return KVQ_OK;
+}
+
+}  // extern "C"

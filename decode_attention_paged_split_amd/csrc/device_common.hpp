@@ -1,0 +1,96 @@
+// Device helpers shared by the kvq kernels (gfx950, wave64).
+//
+// bf16 handling, the round-up conversion used for affine scales, and cross-lane
+// reductions built from DPP row controls and the gfx950 permlane swaps (no LDS traffic).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+// ---------------------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+// low / high bf16 of a packed pair, widened exactly
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// f32 -> bf16, round to nearest, ties to even (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// smallest bf16 >= x (finite x >= 0 in our use; negative handled for completeness)
+__device__ __forceinline__ uint32_t f32_to_bf16_up(float x) {
+  uint32_t r = f32_to_bf16_rne(x);
+  if (bf16_to_f32(r) < x) {
+    if ((r & 0x7FFFu) == 0u) r = 1u;           // +-0 -> smallest positive subnormal
+    else if (r & 0x8000u) r -= 1u;             // negative: toward zero
+    else r += 1u;
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------- lanes
+
+// DPP controls (gfx9 encoding)
+enum : int {
+  DPP_QUAD_1032 = 0xB1,      // quad_perm [1,0,3,2]  (lane ^ 1)
+  DPP_QUAD_2301 = 0x4E,      // quad_perm [2,3,0,1]  (lane ^ 2)
+  DPP_ROW_MIRROR = 0x140,    // lane i <- 15 - i within a row of 16
+  DPP_ROW_HALF_MIRROR = 0x141 // lane i <- 7 - i within each half row of 8
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+struct OpAdd { __device__ static float f(float a, float b) { return a + b; } };
+struct OpMax { __device__ static float f(float a, float b) { return fmaxf(a, b); } };
+
+// One butterfly step at lane distance OFF (a power of two <= 32), combining every lane
+// with a lane of the neighbouring aligned block of OFF lanes.  Steps must be taken in
+// increasing OFF starting from a block size over which the values are already uniform
+// (distance 1 and 2 are exact xor swaps; 4 and 8 use the mirror controls, which pick
+// some lane of the other block -- equal to the xor partner once blocks are uniform).
+template <class OP, int OFF>
+__device__ __forceinline__ float xstep(float x) {
+  if constexpr (OFF == 1) {
+    return OP::f(x, dpp<DPP_QUAD_1032>(x));
+  } else if constexpr (OFF == 2) {
+    return OP::f(x, dpp<DPP_QUAD_2301>(x));
+  } else if constexpr (OFF == 4) {
+    return OP::f(x, dpp<DPP_ROW_HALF_MIRROR>(x));
+  } else if constexpr (OFF == 8) {
+    return OP::f(x, dpp<DPP_ROW_MIRROR>(x));
+  } else if constexpr (OFF == 16) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return OP::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    static_assert(OFF == 32, "lane distance");
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return OP::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+}
+
+// All-reduce over aligned blocks of HI lanes, assuming values are uniform over aligned
+// blocks of LO lanes (LO, HI powers of two, 1 <= LO <= HI <= 64).  Every lane of a block
+// ends with the block's result.
+template <class OP, int LO, int HI>
+__device__ __forceinline__ float block_reduce(float x) {
+  if constexpr (LO < HI) {
+    x = xstep<OP, LO>(x);
+    return block_reduce<OP, LO * 2, HI>(x);
+  } else {
+    return x;
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace kvq

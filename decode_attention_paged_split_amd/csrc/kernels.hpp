@@ -1,0 +1,65 @@
+// Kernel argument blocks and launchers of the kvq library (host and device visible).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+struct AppendArgs {
+  const uint16_t* k;      // [T, HK, D] bf16
+  const uint16_t* v;
+  const int64_t* slots;   // [T]
+  void* k_plane;          // codes (uint32) or bf16 values
+  void* v_plane;
+  void* k_scale;          // bf16 planes (affine only)
+  void* k_bias;
+  void* v_scale;
+  void* v_bias;
+  int32_t T, HK, D, BS;
+  int64_t num_slots;      // num_blocks * BS
+};
+
+struct GatherArgs {
+  const uint8_t* plane;   // one pool plane
+  uint8_t* out;           // [B, HK, max_len, row_bytes]
+  const int32_t* table;
+  const int32_t* lengths;
+  int32_t B, HK, BS, max_blocks, max_len, num_blocks;
+  int32_t row_bytes;      // bytes of one row of this plane (a multiple of 2)
+};
+
+struct PartialArgs {
+  const uint16_t* q;        // [B, HQ, N, D] bf16
+  const void* k;            // code plane (uint32) or bf16 values
+  const void* v;
+  const uint16_t* ks;       // [NB, HK, BS, G] bf16 (affine only)
+  const uint16_t* kb;
+  const uint16_t* vs;
+  const uint16_t* vb;
+  const int32_t* table;     // [B, max_blocks]
+  const int32_t* lengths;   // [B]
+  float* opart;             // [B, HQ, N, P, D] f32, unnormalised
+  float* ml;                // [B, HQ, N, P, 2] f32: running max (log2 units), normaliser
+  float scale_log2e;        // softmax scale * log2(e)
+  int32_t HQ, HK, N, BS, bs_shift, max_blocks, num_blocks, max_len;
+  int32_t part_tokens, num_parts, qgroups;
+};
+
+struct MergeArgs {
+  const float* opart;
+  const float* ml;
+  const int32_t* lengths;
+  void* out;                // [B, HQ, N, D] bf16 or f32
+  int32_t HQ, N, D, part_tokens, num_parts, out_f32, max_len;
+};
+
+hipError_t launch_append(const AppendArgs& a, int bits, hipStream_t stream);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
+
+// qvw: query vectors per workgroup (REP * N split into qgroups groups of qvw)
+hipError_t launch_partial(const PartialArgs& a, int bits, int D, int qvw, int B, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t stream);
+bool partial_supported(int bits, int D, int qvw);
+
+}  // namespace kvq

@@ -1,0 +1,177 @@
+/*
+ * kvq.h -- paged, split-K decode attention over bf16 or affine-quantized KV pages,
+ * for AMD Instinct MI355X (gfx950).  Plain C ABI: pointers, sizes and status codes; no
+ * HIP or PyTorch types appear in any signature (the stream is an opaque `void*` that
+ * holds a hipStream_t; NULL means the default stream).
+ *
+ * Pages this interface follows (the text of four npm-diff web pages):
+ *   [P50]  "@mlx-bun/inference 0.0.0-stage -> 1.0.0", diff page 50:
+ *          src/kernels/attention/kvq4-decode.ts, paged.ts, multi-query.ts
+ *   [P134] "@mlx-bun/inference 0.0.0-stage -> 1.0.0", diff page 134:
+ *          src/state/paged/cache.ts
+ *   [P47]  "mlx-bun 0.2.0 -> 0.4.0", diff page 47: model/batched-quantized-kv.ts
+ *
+ * Conventions shared by every entry point
+ *   - Return value: KVQ_OK (0) or a negative kvq_status.  A failing call enqueues
+ *     nothing; kvq_last_error() then returns a message for the calling thread.
+ *   - Device pointers are borrowed for the stream-ordered duration of the call; the
+ *     library never frees caller memory.  All tensors are dense, row-major, in the
+ *     layouts stated below.
+ *   - Calls enqueue work on `stream` and return without synchronising.  The only
+ *     synchronous errors are argument checks; a device fault surfaces at the caller's
+ *     next synchronisation.
+ *   - bf16 values travel as their 16-bit patterns (uint16_t).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID = -1,      /* bad argument: null pointer, shape, size */
+  KVQ_ERR_UNSUPPORTED = -2,  /* a format or shape this library does not read directly */
+  KVQ_ERR_OOM = -3,          /* device allocation failed */
+  KVQ_ERR_HIP = -4,          /* a HIP runtime call failed (message has the HIP error) */
+  KVQ_ERR_WORKSPACE = -5,    /* workspace smaller than paged_decode_workspace_bytes() */
+  KVQ_ERR_RANGE = -6         /* a size beyond the pool (the pages' PagedPoolExhausted) */
+} kvq_status;
+
+/* Pool planes, each shaped [num_blocks, num_kv_heads, block_size, width] ([P134]
+ * cache.ts, class BlockPool).  bf16 pages (bits == 16) have only K and V (uint16, width
+ * head_dim).  Affine pages have packed codes K and V (uint32, width head_dim*bits/32,
+ * element i of a row in bits [bits*(i%P), bits*(i%P+1)) of word i/P, P = 32/bits:
+ * [P50] paged.ts, paged_attention_affine_partial) and bf16 scale and bias planes of
+ * width head_dim/group_size. */
+typedef enum kvq_plane {
+  KVQ_PLANE_K = 0,
+  KVQ_PLANE_V = 1,
+  KVQ_PLANE_K_SCALE = 2,
+  KVQ_PLANE_K_BIAS = 3,
+  KVQ_PLANE_V_SCALE = 4,
+  KVQ_PLANE_V_BIAS = 5
+} kvq_plane;
+#define KVQ_NUM_PLANES 6
+
+typedef struct kvq_pool_desc {
+  int32_t num_blocks;    /* physical blocks NB >= 1 */
+  int32_t num_kv_heads;  /* HK >= 1 */
+  int32_t block_size;    /* tokens per block BS >= 1 */
+  int32_t head_dim;      /* D, a multiple of group_size, at most 256 */
+  int32_t bits;          /* 16 = bf16 pages; 8, 4 or 2 = affine codes (32 % bits == 0) */
+  int32_t group_size;    /* elements per scale/bias group along the head dim: 64 */
+} kvq_pool_desc;
+
+typedef struct kvq_pool kvq_pool;  /* opaque */
+
+/* Bytes of one plane of a pool with this descriptor (0 for a plane the format lacks or
+ * an invalid descriptor). */
+size_t kv_pool_plane_bytes(const kvq_pool_desc* desc, int32_t plane);
+
+/* Create a pool whose planes the library allocates on the current device and fills with
+ * zeros (the pages' pool starts as ops.zeros: [P134] BlockPool constructor).  The library
+ * owns the planes until kv_pool_destroy.  Errors: KVQ_ERR_INVALID (descriptor),
+ * KVQ_ERR_UNSUPPORTED (bits/group), KVQ_ERR_OOM. */
+int kv_pool_create(const kvq_pool_desc* desc, kvq_pool** out);
+
+/* Create a pool over planes the caller allocated (planes[p] for every plane the format
+ * has, each at least kv_pool_plane_bytes(desc, p) bytes, 16-byte aligned; entries for
+ * absent planes are ignored).  The caller keeps ownership; kv_pool_destroy frees only the
+ * handle.  Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED. */
+int kv_pool_wrap(const kvq_pool_desc* desc, void* const planes[KVQ_NUM_PLANES], kvq_pool** out);
+
+/* Release a pool handle (and its planes if the library allocated them).  NULL is a no-op.
+ * Work still queued on a stream that reads the pool must finish first. */
+int kv_pool_destroy(kvq_pool* pool);
+
+/* Device address and size of one plane.  Errors: KVQ_ERR_INVALID for a plane the format
+ * lacks. */
+int kv_pool_plane(const kvq_pool* pool, int32_t plane, void** dev_ptr, size_t* bytes);
+
+/* Copy a pool's descriptor out. */
+int kv_pool_describe(const kvq_pool* pool, kvq_pool_desc* out);
+
+/* Quantize-on-append ([P134] cache.ts, BlockPool.writeBlock and PagedKVCache.append):
+ * write T new K/V rows into the pool, quantizing affine pages per (token, head, group of
+ * group_size elements):  mn, mx = min, max; scale = (mx - mn) / (2^bits - 1) in f32,
+ * rounded up to bf16; bias = mn; code = clamp(rint((x - bias) / scale), 0, 2^bits - 1)
+ * (round half to even; a group with scale 0 stores code 0); codes packed low-first.
+ *   k, v   device bf16 [T, num_kv_heads, head_dim]
+ *   slots  device int64 [T]: physical slot = block * block_size + row; a negative slot
+ *          skips its row; a slot >= num_blocks * block_size is skipped as well.
+ * Rows of one call must target distinct slots.  T == 0 is a no-op. */
+int kv_append_quantize(kvq_pool* pool, const uint16_t* k, const uint16_t* v,
+                       const int64_t* slots, int32_t num_tokens, void* stream);
+
+typedef struct kvq_decode_shape {
+  int32_t batch;               /* B sequences */
+  int32_t num_q_heads;         /* HQ, a multiple of the pool's HK */
+  int32_t q_rows;              /* N query rows per sequence, 1..8 */
+  int32_t max_blocks_per_seq;  /* columns of block_table */
+  int32_t max_len;             /* host upper bound on every lengths[b] (sizes the grid) */
+  int32_t partition_tokens;    /* tokens per split-K partition; 0 = automatic */
+  int32_t out_f32;             /* 0: out is bf16; 1: out is f32 (unrounded merge result) */
+} kvq_decode_shape;
+
+/* Bytes of workspace paged_decode_attention needs for this shape (0 if the shape is
+ * invalid).  The workspace holds per-partition partial outputs (f32). */
+size_t paged_decode_workspace_bytes(const kvq_pool* pool, const kvq_decode_shape* shape);
+
+/* Partition size the library picks for partition_tokens == 0 (for reporting). */
+int32_t paged_decode_partition_tokens(const kvq_pool* pool, const kvq_decode_shape* shape);
+
+/* Decode attention for N <= 8 query rows per sequence read straight from the pages
+ * ([P50] paged.ts pagedAttentionView.attend, direct route; kvq4-decode.ts):
+ *   out[b, h, i, :] = sum_t softmax_t(scale * q[b,h,i,:] . K[b,t,g,:]) V[b,t,g,:]
+ * over t < lengths[b] - N + i + 1, with g = h / (HQ / HK) (GQA), K and V the dequantized
+ * page rows (scale * code + bias in f32) or the bf16 rows.  Token t of sequence b sits in
+ * block block_table[b, t / BS], row t % BS.  Computed as a split-K partial pass (online
+ * softmax in f32 per partition, every K/V row read once for all HQ/HK heads of its
+ * group) followed by a log-sum-exp merge.
+ *   q            device bf16 [B, HQ, N, head_dim]
+ *   block_table  device int32 [B, max_blocks_per_seq]; entries past ceil(len/BS) unread
+ *   lengths      device int32 [B]; each in [N, max_len] (tokens cached, counting the N
+ *                new rows); not checked on the device
+ *   workspace    device, >= paged_decode_workspace_bytes(pool, shape) bytes
+ *   out          device [B, HQ, N, head_dim], bf16 (round to nearest even) or f32
+ * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED (N > 8, HQ % HK != 0),
+ * KVQ_ERR_WORKSPACE. */
+int paged_decode_attention(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table,
+                           const int32_t* lengths, float scale, const kvq_decode_shape* shape,
+                           void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/* The two halves of paged_decode_attention, for callers that time or exchange partials
+ * (e.g. a context-parallel split that merges partials gathered from several devices):
+ * paged_decode_partial writes the per-partition (o, m, l) partials into the workspace;
+ * paged_decode_merge combines them into out ([P50] paged.ts paged_attention_merge).  Same
+ * arguments, layouts and errors as paged_decode_attention; the merge must be given the
+ * same shape (and partition size) the partial pass used. */
+int paged_decode_partial(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table,
+                         const int32_t* lengths, float scale, const kvq_decode_shape* shape,
+                         void* workspace, size_t workspace_bytes, void* stream);
+int paged_decode_merge(const kvq_pool* pool, const int32_t* lengths, const kvq_decode_shape* shape,
+                       const void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/* The fetch copy, for indexing tests ([P134] cache.ts pickBlocks / BlockPool.gather):
+ * every plane's rows of each sequence in token order.  out_planes[p] (device) receives
+ * plane p as [B, num_kv_heads, max_len, width_p] in the plane's element type; rows at
+ * t >= lengths[b] are written as zero.  Entries for absent planes are ignored. */
+int kv_gather_debug(const kvq_pool* pool, const int32_t* block_table, const int32_t* lengths,
+                    int32_t batch, int32_t max_blocks_per_seq, int32_t max_len,
+                    void* const out_planes[KVQ_NUM_PLANES], void* stream);
+
+/* Message for the calling thread's last failing call ("" if none). */
+const char* kvq_last_error(void);
+
+/* Library version string. */
+const char* kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -1,0 +1,134 @@
+"""The C-ABI library loads, exports every entry point include/kvq.h declares, and rejects bad
+arguments on the host (CPU only: no call here launches a kernel)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import decode_attention_paged_split_amd as kvq
+from workloads import make_workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|int32_t|size_t|char\s*\*|void)\s*\**\s*(\w+)\s*\(", src, re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kvq.LIB_PATH):
+        pytest.skip("libkvq.so not built (python -m decode_attention_paged_split_amd.build)")
+    return kvq.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for must in ["kv_pool_create", "kv_pool_destroy", "kv_append_quantize", "paged_decode_attention",
+                 "paged_decode_workspace_bytes", "kv_gather_debug", "kvq_last_error"]:
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in _declared():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_struct_layouts():
+    assert ctypes.sizeof(kvq.PoolDesc) == 24
+    assert ctypes.sizeof(kvq.DecodeShape) == 28
+
+
+@pytest.mark.parametrize("name,expect", [("c3", 345157632), ("c2", 139984896), ("c1", 1179648),
+                                         ("c5", 1522151424), ("c4_8", 1140850688), ("c4_2", 335544320)])
+def test_pool_bytes_match_the_layout(lib, name, expect):
+    """Pool sizes [NB, HK, BS, width] per plane for the seeded workloads."""
+    w = make_workload(name)
+    d = kvq.PoolDesc(w.num_blocks, w.HK, w.BS, w.D, w.bits, 64)
+    total = sum(kvq.kv_pool_plane_bytes(d, p) for p in range(6))
+    assert total == expect
+    rows = w.num_blocks * w.HK * w.BS
+    if w.bits == 16:
+        assert kvq.kv_pool_plane_bytes(d, 0) == rows * w.D * 2
+        assert kvq.kv_pool_plane_bytes(d, 2) == 0
+    else:
+        assert kvq.kv_pool_plane_bytes(d, 0) == rows * w.D * w.bits // 8
+        assert kvq.kv_pool_plane_bytes(d, 5) == rows * (w.D // 64) * 2
+
+
+@pytest.mark.parametrize("field,value,code", [("bits", 3, -2), ("bits", 32, -2), ("group_size", 32, -2),
+                                              ("head_dim", 96, -2), ("head_dim", 512, -2),
+                                              ("num_blocks", 0, -1), ("block_size", 0, -1)])
+def test_pool_descriptor_rejected(lib, field, value, code):
+    d = kvq.PoolDesc(4, 2, 16, 128, 4, 64)
+    setattr(d, field, value)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kv_pool_wrap(d, [16] * 6)
+    assert e.value.code == code
+    assert lib.kvq_last_error().decode()
+
+
+class _FakePool:
+    def __init__(self, bits=4, HK=2, BS=32, D=256, NB=64):
+        self.desc = kvq.PoolDesc(NB, HK, BS, D, bits, 64)
+        self.handle = kvq.kv_pool_wrap(self.desc, [256] * 6)   # host-side handle only
+
+    def close(self):
+        kvq.kv_pool_destroy(self.handle)
+
+
+@pytest.mark.parametrize("mut,code", [(dict(q_rows=9), -2), (dict(q_rows=0), -2), (dict(num_q_heads=5), -2),
+                                      (dict(batch=0), -1), (dict(max_len=0), -1),
+                                      (dict(max_blocks_per_seq=1, max_len=1000), -6),
+                                      (dict(partition_tokens=-1), -1)])
+def test_decode_shape_rejected(lib, mut, code):
+    p = _FakePool()
+    s = kvq.DecodeShape(2, 16, 1, 40, 1000, 0, 0)
+    for k, v in mut.items():
+        setattr(s, k, v)
+    assert lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s)) == 0
+    rc = lib.paged_decode_attention(ctypes.c_void_p(256), p.handle, ctypes.c_void_p(256), ctypes.c_void_p(256),
+                                    1.0, ctypes.byref(s), ctypes.c_void_p(256), 1 << 30, ctypes.c_void_p(256),
+                                    None)
+    assert rc == code, lib.kvq_last_error()
+    p.close()
+
+
+def test_workspace_too_small_and_null_pointers(lib):
+    p = _FakePool()
+    s = kvq.DecodeShape(2, 16, 1, 40, 1000, 256, 0)
+    need = lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s))
+    # partials: B*HQ*N*ceil(1000/256) rows of (D + 2) floats (o block padded to 256 B)
+    parts = 4
+    o = 2 * 16 * parts * 256 * 4
+    assert need == ((o + 255) // 256) * 256 + 2 * 16 * parts * 2 * 4
+    rc = lib.paged_decode_attention(ctypes.c_void_p(256), p.handle, ctypes.c_void_p(256), ctypes.c_void_p(256),
+                                    1.0, ctypes.byref(s), ctypes.c_void_p(256), need - 1, ctypes.c_void_p(256),
+                                    None)
+    assert rc == -5
+    rc = lib.paged_decode_attention(None, p.handle, ctypes.c_void_p(256), ctypes.c_void_p(256), 1.0,
+                                    ctypes.byref(s), ctypes.c_void_p(256), need, ctypes.c_void_p(256), None)
+    assert rc == -1
+    rc = lib.kv_append_quantize(p.handle, None, ctypes.c_void_p(256), ctypes.c_void_p(256), 4, None)
+    assert rc == -1
+    assert lib.kv_append_quantize(p.handle, None, None, None, 0, None) == 0     # T == 0 is a no-op
+    p.close()
+
+
+def test_automatic_partition_is_a_power_of_two(lib):
+    p = _FakePool()
+    s = kvq.DecodeShape(32, 16, 1, 1100, 32197, 0, 0)
+    pt = lib.paged_decode_partition_tokens(p.handle, ctypes.byref(s))
+    assert pt >= 64 and pt & (pt - 1) == 0
+    s.partition_tokens = 300
+    assert lib.paged_decode_partition_tokens(p.handle, ctypes.byref(s)) == 300
+    p.close()

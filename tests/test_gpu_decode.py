@@ -1,0 +1,129 @@
+"""GPU: paged decode attention (partial + merge) against the f64 oracle.
+
+Tolerances: the f32 output (out_f32=1) is within max abs 2e-3 and relative L2 2e-3 of the
+oracle; the bf16 output is exactly the round-to-nearest-even of the f32 output, and within
+rel L2 2e-3 / max abs max(2e-3, one bf16 ulp of the reference) of the oracle.  The shapes
+below are the workloads' own shapes at reduced batch and length (several partitions and a
+ragged tail), plus edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_paged_split_amd as kvq
+from oracle import attention
+from tests import gpu_util as G
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "c1": dict(),                                                    # full size: 1 x 2048
+    "c2": dict(B=3, len_lo=100, len_hi=900),
+    "c3": dict(B=4, len_lo=300, len_hi=2100),
+    "c4_8": dict(B=2, len_lo=3000, len_hi=3000),
+    "c4_2": dict(B=2, len_lo=3000, len_hi=3000),
+    "c5": dict(B=3, len_lo=500, len_hi=1500),
+}
+
+
+@pytest.fixture(scope="module")
+def filled():
+    cache = {}
+
+    def get(name, **kw):
+        key = (name, tuple(sorted(kw.items())))
+        if key not in cache:
+            w = make_workload(name, **kw)
+            pool = G.new_pool(w)
+            G.fill_pool(w, pool)
+            cache[key] = (w, pool, attention.workload_output(w))
+        return cache[key]
+    yield get
+    for w, pool, _ in cache.values():
+        pool.close()
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("pt", [0, 64, 333])
+def test_decode_parity(filled, name, pt):
+    print(f"decode {name} pt={pt}", flush=True)
+    w, pool, ref = filled(name, **SMALL[name])
+    got = G.run_decode(w, pool, partition_tokens=pt, out_f32=True)
+    G.check_f32(got, ref, tag=f"{name} pt={pt}")
+    bits = G.run_decode(w, pool, partition_tokens=pt, out_f32=False)
+    assert np.array_equal(bits, G.rne_f32_to_bf16(got)), "bf16 output must be RNE of the f32 output"
+    G.check_bf16(bits, ref, tag=f"{name} pt={pt}")
+
+
+def test_partition_count_invariance(filled):
+    """c4 shapes: 1, 16 and 256 partitions of one 3072-token sequence agree to rel L2 1e-5."""
+    w, pool, ref = filled("c4_2", B=1, len_lo=3072, len_hi=3072)
+    outs = [G.run_decode(w, pool, partition_tokens=pt) for pt in (3072, 192, 12)]
+    for o in outs[1:]:
+        assert np.linalg.norm(o - outs[0]) / np.linalg.norm(outs[0]) <= 1e-5
+    G.check_f32(outs[0], ref)
+
+
+def test_deterministic(filled):
+    w, pool, _ = filled("c3", **SMALL["c3"])
+    a = G.run_decode(w, pool)
+    b = G.run_decode(w, pool)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("case", [
+    dict(name="c5", B=2, len_lo=4, len_hi=4),            # only the N new rows are cached
+    dict(name="c3", B=3, len_lo=1, len_hi=3),            # one to three tokens
+    dict(name="c3", B=2, len_lo=32, len_hi=32),          # exactly one block
+    dict(name="c2", B=2, len_lo=15, len_hi=17),          # around one block of 16
+    dict(name="c3", B=1, len_lo=5000, len_hi=5000, HQ=2, HK=2),      # REP 1
+    dict(name="c5", B=2, len_lo=300, len_hi=700, N=8, HQ=16, HK=2),  # 8 rows x REP 8 = 64 vectors
+    dict(name="c5", B=2, len_lo=300, len_hi=700, N=3, HQ=6, HK=2),   # 3 rows x REP 3
+    dict(name="c2", B=2, len_lo=200, len_hi=900, D=64, HQ=8, HK=4),  # head dim 64, bf16 pages
+    dict(name="c4_2", B=2, len_lo=200, len_hi=900, D=64),            # head dim 64, 2-bit
+    dict(name="c4_8", B=2, len_lo=200, len_hi=900, D=256, HQ=4, HK=1),
+])
+def test_decode_edge_cases(filled, case):
+    case = dict(case)
+    name = case.pop("name")
+    print(f"edge {name} {case}", flush=True)
+    w, pool, ref = filled(name, **case)
+    for pt in (0, 7):
+        got = G.run_decode(w, pool, partition_tokens=pt)
+        G.check_f32(got, ref, tag=f"{name} {case} pt={pt}")
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4_8"])
+def test_poisoned_tail_and_free_blocks_are_not_read(filled, name):
+    """Rows past each length in its last block, and every block no sequence owns, are set to NaN
+    (bf16 pages) or given NaN scales and biases (affine pages): the output must not change."""
+    w, pool, ref = filled(name, **SMALL[name])
+    clean = G.run_decode(w, pool)
+    used = np.zeros((w.num_blocks, w.BS), bool)
+    for b in range(w.B):
+        t = np.arange(int(w.lengths[b]))
+        used[w.table[b, t // w.BS], t % w.BS] = True
+    extra = 3
+    pp = kvq.Pool(w.num_blocks + extra, w.HK, w.BS, w.D, w.bits)
+    for n, t in pool.planes.items():
+        pp.planes[n][: w.num_blocks].copy_(t)
+    mask = torch.from_numpy(np.concatenate([~used, np.ones((extra, w.BS), bool)])).to("cuda")
+    mask = mask[:, None, :].expand(-1, w.HK, -1)
+    nan_bf16 = torch.tensor(0x7FC0, dtype=torch.int16, device="cuda")
+    names = ["k", "v"] if w.bits == 16 else ["k_scale", "k_bias", "v_scale", "v_bias"]
+    for n in names:
+        pp.planes[n].masked_fill_(mask[..., None].expand_as(pp.planes[n]), nan_bf16)
+    got = G.run_decode(w, pp)
+    assert np.array_equal(got, clean)
+    pp.close()
+
+
+def test_bad_table_entry_does_not_fault(filled):
+    """A table entry out of range is clamped on the device (the result is unspecified, the
+    kernel must not read outside the pool)."""
+    w, pool, _ = filled("c3", **SMALL["c3"])
+    table = w.table.copy()
+    table[0, 0] = w.num_blocks + 1000
+    table[1, 1] = -7
+    got = G.run_decode(w, pool, table=G.i32_dev(table))
+    assert got.shape == (w.B, w.HQ, w.N, w.D)
