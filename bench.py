@@ -40,7 +40,7 @@ def log(*a):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("decode.hip", "device_common.hpp", "kernels.hpp"):
+    for f in ("partial_valu.hip", "device_common.hpp", "kernels.hpp"):
         with open(os.path.join(ROOT, "decode_attention_paged_split_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -54,7 +55,8 @@ int validate_desc(const kvq_pool_desc* d) {
   if (d->head_dim % 64 != 0 || d->head_dim > 256)
     return fail(KVQ_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256, got %d", d->head_dim);
   const size_t rows = (size_t)d->num_blocks * d->num_kv_heads * d->block_size;
-  if (rows > (size_t)1 << 40) return fail(KVQ_ERR_INVALID, "pool too large");
+  if (rows >= (size_t)1 << 31)
+    return fail(KVQ_ERR_UNSUPPORTED, "num_blocks * num_kv_heads * block_size must stay below 2^31 rows");
   return KVQ_OK;
 }
 
@@ -81,32 +83,33 @@ int device_cus() {
 
 constexpr int MAX_PARTS = 8192;
 
-int qvw_for(int qv) {
-  for (int w = 8; w >= 1; w /= 2)
+// query vectors per workgroup: the largest power of two <= 8 dividing REP * N (<= 4 for 2-bit
+// pages, whose V lanes hold 16 dims each)
+int qvw_for(int qv, int bits) {
+  for (int w = (bits == 2 ? 4 : 8); w >= 1; w /= 2)
     if (qv % w == 0) return w;
   return 1;
 }
 
-// Tokens per split-K partition: the smallest power of two >= 64 for which the upper bound
-// on workgroups (every sequence at max_len) stays within 8 per compute unit, so that the
-// grid fills the chip while partial traffic stays small.  KVQ_PARTITION_TOKENS overrides.
+// Tokens per split-K partition for the fixed-partition schedule; 0 selects the balanced
+// stream schedule (every wave gets an equal share of all cached tokens).  KVQ_PARTITION_TOKENS
+// (> 0) overrides an automatic choice, for sweeps.
 int choose_partition(const kvq_pool* pool, const kvq_decode_shape* s) {
+  (void)pool;
   if (s->partition_tokens > 0) return s->partition_tokens;
   if (const char* e = std::getenv("KVQ_PARTITION_TOKENS")) {
     const int v = std::atoi(e);
     if (v > 0) return v;
   }
-  const int hk = pool->desc.num_kv_heads;
-  const int qv = (s->num_q_heads / hk) * s->q_rows;
-  const int qg = qv / qvw_for(qv);
-  const long budget = 8L * device_cus();
-  int pt = 64;
-  while (pt < (1 << 20)) {
-    const long parts = (s->max_len + pt - 1) / pt;
-    if ((long)s->batch * hk * qg * parts <= budget && parts <= MAX_PARTS) break;
-    pt *= 2;
-  }
-  return pt;
+  return 0;
+}
+
+// waves the stream schedule launches: 8 per compute unit (two per SIMD), all resident at once
+int stream_waves() { return 8 * device_cus(); }
+
+int qgroups_of(const kvq_pool* pool, const kvq_decode_shape* s) {
+  const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
+  return qv / qvw_for(qv, pool->desc.bits);
 }
 
 int validate_shape(const kvq_pool* pool, const kvq_decode_shape* s) {
@@ -127,22 +130,34 @@ int validate_shape(const kvq_pool* pool, const kvq_decode_shape* s) {
                 (long)s->max_blocks_per_seq * pool->desc.block_size);
   if (s->partition_tokens < 0) return fail(KVQ_ERR_INVALID, "partition_tokens must be >= 0");
   const int pt = choose_partition(pool, s);
-  if ((s->max_len + pt - 1) / pt > MAX_PARTS)
+  if (pt > 0 && (s->max_len + pt - 1) / pt > MAX_PARTS)
     return fail(KVQ_ERR_UNSUPPORTED, "more than %d partitions (max_len %d, partition %d)", MAX_PARTS,
                 s->max_len, pt);
+  if ((double)s->batch * s->max_len * pool->desc.num_kv_heads * qgroups_of(pool, s) >= 1099511627776.0)
+    return fail(KVQ_ERR_UNSUPPORTED, "batch * max_len * num_kv_heads * query groups must stay below 2^40");
   const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
-  if (!kvq::partial_supported(pool->desc.bits, pool->desc.head_dim, qvw_for(qv)))
+  if (!kvq::partial_supported(pool->desc.bits, pool->desc.head_dim, qvw_for(qv, pool->desc.bits)))
     return fail(KVQ_ERR_UNSUPPORTED, "no kernel for bits=%d D=%d", pool->desc.bits, pool->desc.head_dim);
   return KVQ_OK;
 }
 
+// Partials: fixed partitions hold [B, HQ, N, parts] rows; the stream schedule holds
+// (waves + units) slots of QVW vectors (slot = unit + wave).  Each partial row is D floats of
+// unnormalised output plus (max, normaliser).
 size_t workspace_layout(const kvq_pool* pool, const kvq_decode_shape* s, int pt, size_t* ml_off) {
-  const size_t parts = (size_t)(s->max_len + pt - 1) / pt;
-  const size_t rows = (size_t)s->batch * s->num_q_heads * s->q_rows;
-  size_t o_bytes = rows * parts * pool->desc.head_dim * sizeof(float);
+  size_t rows;
+  if (pt > 0) {
+    const size_t parts = (size_t)(s->max_len + pt - 1) / pt;
+    rows = (size_t)s->batch * s->num_q_heads * s->q_rows * parts;
+  } else {
+    const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
+    const size_t units = (size_t)s->batch * pool->desc.num_kv_heads * qgroups_of(pool, s);
+    rows = ((size_t)stream_waves() + units) * qvw_for(qv, pool->desc.bits);
+  }
+  size_t o_bytes = rows * pool->desc.head_dim * sizeof(float);
   o_bytes = (o_bytes + 255) & ~(size_t)255;
   *ml_off = o_bytes;
-  return o_bytes + rows * parts * 2 * sizeof(float);
+  return o_bytes + rows * 2 * sizeof(float);
 }
 
 }  // namespace
@@ -286,9 +301,9 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   if (workspace_bytes < need)
     return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   const kvq_pool_desc& d = pool->desc;
-  const int parts = (shape->max_len + pt - 1) / pt;
+  const int parts = pt > 0 ? (shape->max_len + pt - 1) / pt : 0;
   const int qv = (shape->num_q_heads / d.num_kv_heads) * shape->q_rows;
-  P->qvw = qvw_for(qv);
+  P->qvw = qvw_for(qv, pool->desc.bits);
 
   kvq::PartialArgs& a = P->a;
   a = kvq::PartialArgs{};
@@ -308,12 +323,17 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
     if ((1 << s) == d.block_size) a.bs_shift = s;
   a.max_blocks = shape->max_blocks_per_seq; a.num_blocks = d.num_blocks; a.max_len = shape->max_len;
   a.part_tokens = pt; a.num_parts = parts; a.qgroups = qv / P->qvw;
+  a.len_cap = (int)std::min<long>(shape->max_len, (long)shape->max_blocks_per_seq * d.block_size);
+  a.batch = shape->batch; a.num_waves = stream_waves(); a.min_tokens = kvq::tile_tokens(d.bits, d.head_dim);
 
   kvq::MergeArgs& m = P->m;
   m = kvq::MergeArgs{};
   m.opart = a.opart; m.ml = a.ml; m.lengths = lengths; m.out = out;
   m.HQ = shape->num_q_heads; m.N = shape->q_rows; m.D = d.head_dim; m.part_tokens = pt;
   m.num_parts = parts; m.out_f32 = shape->out_f32 ? 1 : 0; m.max_len = shape->max_len;
+  m.len_cap = a.len_cap;
+  m.batch = shape->batch; m.HK = d.num_kv_heads; m.qgroups = a.qgroups; m.qvw = P->qvw;
+  m.num_waves = a.num_waves; m.min_tokens = a.min_tokens;
   return KVQ_OK;
 }
 

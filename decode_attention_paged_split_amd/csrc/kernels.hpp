@@ -43,7 +43,13 @@ struct PartialArgs {
   float* ml;                // [B, HQ, N, P, 2] f32: running max (log2 units), normaliser
   float scale_log2e;        // softmax scale * log2(e)
   int32_t HQ, HK, N, BS, bs_shift, max_blocks, num_blocks, max_len;
-  int32_t part_tokens, num_parts, qgroups;
+  int32_t part_tokens;      // > 0: fixed partitions of this many tokens; 0: balanced stream
+  int32_t num_parts;        // fixed partitions: partitions per sequence (grid x)
+  int32_t qgroups;          // query groups of QVW vectors per KV head
+  int32_t batch;
+  int32_t num_waves;        // stream: waves launched
+  int32_t min_tokens;       // stream: fewest tokens per working wave (one tile)
+  int32_t len_cap;          // min(max_len, max_blocks * BS): lengths are clamped to [0, len_cap]
 };
 
 struct MergeArgs {
@@ -52,6 +58,8 @@ struct MergeArgs {
   const int32_t* lengths;
   void* out;                // [B, HQ, N, D] bf16 or f32
   int32_t HQ, N, D, part_tokens, num_parts, out_f32, max_len;
+  int32_t len_cap;          // min(max_len, max_blocks * BS): lengths are clamped to [0, len_cap]
+  int32_t batch, HK, qgroups, qvw, num_waves, min_tokens;   // stream schedule (part_tokens == 0)
 };
 
 hipError_t launch_append(const AppendArgs& a, int bits, hipStream_t stream);
@@ -61,5 +69,6 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_partial(const PartialArgs& a, int bits, int D, int qvw, int B, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t stream);
 bool partial_supported(int bits, int D, int qvw);
+int tile_tokens(int bits, int D);
 
 }  // namespace kvq

@@ -124,11 +124,18 @@ def test_workspace_too_small_and_null_pointers(lib):
     p.close()
 
 
-def test_automatic_partition_is_a_power_of_two(lib):
+def test_automatic_schedule_is_the_balanced_stream(lib, monkeypatch):
+    """partition_tokens == 0 selects the balanced stream schedule (reported as 0 tokens); its
+    workspace holds (waves + units) partial slots of the workgroup's query vectors."""
+    monkeypatch.delenv("KVQ_PARTITION_TOKENS", raising=False)
     p = _FakePool()
     s = kvq.DecodeShape(32, 16, 1, 1100, 32197, 0, 0)
-    pt = lib.paged_decode_partition_tokens(p.handle, ctypes.byref(s))
-    assert pt >= 64 and pt & (pt - 1) == 0
+    assert lib.paged_decode_partition_tokens(p.handle, ctypes.byref(s)) == 0
+    need = lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s))
+    waves = 8 * 256                                   # no device here: 256 compute units assumed
+    slots = (waves + 32 * 2) * 8                      # units = B * HK (one query group of 8)
+    o = slots * 256 * 4
+    assert need == ((o + 255) // 256) * 256 + slots * 2 * 4
     s.partition_tokens = 300
     assert lib.paged_decode_partition_tokens(p.handle, ctypes.byref(s)) == 300
     p.close()

@@ -127,3 +127,17 @@ def test_bad_table_entry_does_not_fault(filled):
     table[1, 1] = -7
     got = G.run_decode(w, pool, table=G.i32_dev(table))
     assert got.shape == (w.B, w.HQ, w.N, w.D)
+
+
+def test_precondition_violations_do_not_fault_or_leak(filled):
+    """A zero length and a length above max_len break the documented preconditions: the kernels
+    must still stay in bounds, and every other sequence's output must be unchanged."""
+    w, pool, ref = filled("c3", **SMALL["c3"])
+    lengths = w.lengths.astype(np.int32).copy()
+    lengths[1] = 0
+    lengths[2] = w.max_len + 500
+    for pt in (0, 64):
+        got = G.run_decode(w, pool, partition_tokens=pt, lengths=G.i32_dev(lengths))
+        keep = [0] + list(range(3, w.B))
+        G.check_f32(got[keep], ref[keep], tag=f"pt={pt}")
+        assert np.all(got[1] == 0)
