@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--cold", action="store_true", help="write 1 GiB before each step (defeats the caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--probe-copy", type=int, default=0, metavar="BYTES",
+                    help="instead: time a plain device copy of BYTES (achievable-bandwidth probe, and the "
+                         "known-size kernel that calibrates the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -128,6 +131,24 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.probe_copy:
+        src = torch.ones(args.probe_copy // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        moved = 2 * src.numel() * 4
+        print(json.dumps({"probe": "copy", "bytes_read": src.numel() * 4, "bytes_written": src.numel() * 4,
+                          "us_per_copy": round(ms * 1e3, 2), "GB_per_s": round(moved / (ms * 1e-3) / 1e9, 1)}))
+        return
 
     t_setup = time.time()
     w = make_workload(args.workload)
