@@ -109,6 +109,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--engine", choices=["auto", "vector", "matrix"], default="auto",
+                    help="partial-pass engine: vector ALU (the default) or matrix cores (4-bit pages)")
     ap.add_argument("--cold", action="store_true", help="write 1 GiB before each step (defeats the caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -171,7 +173,8 @@ def main():
     q = torch.from_numpy(w.q_bits.view(np.int16)).to(dev)
     table = torch.from_numpy(w.table).to(dev)
     lengths = torch.from_numpy(w.lengths.astype(np.int32)).to(dev)
-    shape = kvq.make_shape(pool, w.B, w.HQ, w.N, w.max_blocks, w.max_len, args.partition_tokens, False)
+    engine = {"auto": kvq.ENGINE_AUTO, "vector": kvq.ENGINE_VECTOR, "matrix": kvq.ENGINE_MATRIX}[args.engine]
+    shape = kvq.make_shape(pool, w.B, w.HQ, w.N, w.max_blocks, w.max_len, args.partition_tokens, False, engine)
     ws = torch.empty(kvq.paged_decode_workspace_bytes(pool, shape), dtype=torch.uint8, device=dev)
     out = torch.empty((w.B, w.HQ, w.N, w.D), dtype=torch.bfloat16, device=dev)
     pt = kvq.paged_decode_partition_tokens(pool, shape)
@@ -234,7 +237,7 @@ def main():
                                f"(sum {int(w.lengths.sum())}), BS={w.BS}, HQ={w.HQ}, HK={w.HK}, D={w.D}, "
                                f"N={w.N}" if w.name == "c3" else w.name,
                    "global_batch": w.B, "seq_len": w.max_len, "parallelism": "single GPU",
-                   "partition_tokens": pt, "cold": bool(args.cold)},
+                   "partition_tokens": pt, "cold": bool(args.cold), "engine": args.engine},
         "us_per_step": round(ms_step * 1e3, 2), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "effective_bytes": eff,
         "kernels_us": {"append": round(float(np.mean(app)) * 1e3, 2), "partial": round(part_s * 1e6, 2),

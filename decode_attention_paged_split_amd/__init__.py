@@ -53,7 +53,11 @@ class PoolDesc(ctypes.Structure):
 class DecodeShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("q_rows", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("max_len", ctypes.c_int32),
-                ("partition_tokens", ctypes.c_int32), ("out_f32", ctypes.c_int32)]
+                ("partition_tokens", ctypes.c_int32), ("out_f32", ctypes.c_int32),
+                ("engine", ctypes.c_int32)]
+
+
+ENGINE_AUTO, ENGINE_VECTOR, ENGINE_MATRIX = 0, 1, 2
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -248,12 +252,12 @@ class Pool:
 
 
 def make_shape(pool: Pool, batch: int, num_q_heads: int, q_rows: int, max_blocks: int, max_len: int,
-               partition_tokens: int = 0, out_f32: bool = False) -> DecodeShape:
-    return DecodeShape(batch, num_q_heads, q_rows, max_blocks, max_len, partition_tokens, int(out_f32))
+               partition_tokens: int = 0, out_f32: bool = False, engine: int = ENGINE_AUTO) -> DecodeShape:
+    return DecodeShape(batch, num_q_heads, q_rows, max_blocks, max_len, partition_tokens, int(out_f32), engine)
 
 
 def decode(q, pool: Pool, block_table, lengths, scale: float, max_len: int, partition_tokens: int = 0,
-           out_f32: bool = False, workspace=None, out=None, stream=None):
+           out_f32: bool = False, workspace=None, out=None, stream=None, engine: int = ENGINE_AUTO):
     """Allocate (if not given) workspace and output, then run paged_decode_attention.
 
     q: bf16 [B, HQ, N, D] (torch.bfloat16 or int16 bit patterns); block_table int32 [B, M];
@@ -261,7 +265,7 @@ def decode(q, pool: Pool, block_table, lengths, scale: float, max_len: int, part
     """
     import torch
     B, HQ, N, D = q.shape
-    shape = make_shape(pool, B, HQ, N, block_table.shape[1], max_len, partition_tokens, out_f32)
+    shape = make_shape(pool, B, HQ, N, block_table.shape[1], max_len, partition_tokens, out_f32, engine)
     if workspace is None:
         workspace = torch.empty(paged_decode_workspace_bytes(pool, shape), dtype=torch.uint8,
                                 device=q.device)

@@ -107,9 +107,18 @@ int choose_partition(const kvq_pool* pool, const kvq_decode_shape* s) {
 // waves the stream schedule launches: 8 per compute unit (two per SIMD), all resident at once
 int stream_waves() { return 8 * device_cus(); }
 
+bool use_mfma(const kvq_decode_shape* s) { return s->engine == KVQ_ENGINE_MATRIX; }
+
+// query vectors per workgroup (vector ALU) or per wave (matrix cores, padded to 16)
+int qvw_of(const kvq_pool* pool, const kvq_decode_shape* s) {
+  const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
+  return use_mfma(s) ? kvq::MFMA_QVW : qvw_for(qv, pool->desc.bits);
+}
+
 int qgroups_of(const kvq_pool* pool, const kvq_decode_shape* s) {
   const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
-  return qv / qvw_for(qv, pool->desc.bits);
+  const int w = qvw_of(pool, s);
+  return (qv + w - 1) / w;
 }
 
 int validate_shape(const kvq_pool* pool, const kvq_decode_shape* s) {
@@ -136,8 +145,17 @@ int validate_shape(const kvq_pool* pool, const kvq_decode_shape* s) {
   if ((double)s->batch * s->max_len * pool->desc.num_kv_heads * qgroups_of(pool, s) >= 1099511627776.0)
     return fail(KVQ_ERR_UNSUPPORTED, "batch * max_len * num_kv_heads * query groups must stay below 2^40");
   const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
-  if (!kvq::partial_supported(pool->desc.bits, pool->desc.head_dim, qvw_for(qv, pool->desc.bits)))
+  if (s->engine < KVQ_ENGINE_AUTO || s->engine > KVQ_ENGINE_MATRIX)
+    return fail(KVQ_ERR_INVALID, "engine must be 0 (automatic), 1 (vector ALU) or 2 (matrix cores)");
+  if (use_mfma(s)) {
+    if (!kvq::mfma_supported(pool->desc.bits, pool->desc.head_dim))
+      return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core engine reads 4-bit pages with head_dim 128 or 256");
+    if (pt > 0)
+      return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core engine runs the balanced stream schedule only "
+                                       "(partition_tokens = 0)");
+  } else if (!kvq::partial_supported(pool->desc.bits, pool->desc.head_dim, qvw_for(qv, pool->desc.bits))) {
     return fail(KVQ_ERR_UNSUPPORTED, "no kernel for bits=%d D=%d", pool->desc.bits, pool->desc.head_dim);
+  }
   return KVQ_OK;
 }
 
@@ -150,9 +168,8 @@ size_t workspace_layout(const kvq_pool* pool, const kvq_decode_shape* s, int pt,
     const size_t parts = (size_t)(s->max_len + pt - 1) / pt;
     rows = (size_t)s->batch * s->num_q_heads * s->q_rows * parts;
   } else {
-    const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
     const size_t units = (size_t)s->batch * pool->desc.num_kv_heads * qgroups_of(pool, s);
-    rows = ((size_t)stream_waves() + units) * qvw_for(qv, pool->desc.bits);
+    rows = ((size_t)stream_waves() + units) * qvw_of(pool, s);
   }
   size_t o_bytes = rows * pool->desc.head_dim * sizeof(float);
   o_bytes = (o_bytes + 255) & ~(size_t)255;
@@ -284,7 +301,13 @@ struct Plan {
   kvq::PartialArgs a;
   kvq::MergeArgs m;
   int qvw;
+  bool mfma;
 };
+
+hipError_t launch_plan_partial(const Plan& P, const kvq_pool* pool, int B, hipStream_t st) {
+  if (P.mfma) return kvq::launch_partial_mfma(P.a, pool->desc.head_dim, st);
+  return kvq::launch_partial(P.a, pool->desc.bits, pool->desc.head_dim, P.qvw, B, st);
+}
 
 int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, const int32_t* lengths, float scale,
          const kvq_decode_shape* shape, void* workspace, size_t workspace_bytes, void* out, bool need_q,
@@ -302,8 +325,8 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
     return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   const kvq_pool_desc& d = pool->desc;
   const int parts = pt > 0 ? (shape->max_len + pt - 1) / pt : 0;
-  const int qv = (shape->num_q_heads / d.num_kv_heads) * shape->q_rows;
-  P->qvw = qvw_for(qv, pool->desc.bits);
+  P->qvw = qvw_of(pool, shape);
+  P->mfma = use_mfma(shape);
 
   kvq::PartialArgs& a = P->a;
   a = kvq::PartialArgs{};
@@ -322,9 +345,9 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   for (int s = 0; s < 31; ++s)
     if ((1 << s) == d.block_size) a.bs_shift = s;
   a.max_blocks = shape->max_blocks_per_seq; a.num_blocks = d.num_blocks; a.max_len = shape->max_len;
-  a.part_tokens = pt; a.num_parts = parts; a.qgroups = qv / P->qvw;
+  a.part_tokens = pt; a.num_parts = parts; a.qgroups = qgroups_of(pool, shape);
   a.len_cap = (int)std::min<long>(shape->max_len, (long)shape->max_blocks_per_seq * d.block_size);
-  a.batch = shape->batch; a.num_waves = stream_waves(); a.min_tokens = kvq::tile_tokens(d.bits, d.head_dim);
+  a.batch = shape->batch; a.num_waves = stream_waves(); a.min_tokens = P->mfma ? kvq::MFMA_TILE : kvq::tile_tokens(d.bits, d.head_dim);
 
   kvq::MergeArgs& m = P->m;
   m = kvq::MergeArgs{};
@@ -345,8 +368,7 @@ int paged_decode_partial(const uint16_t* q, const kvq_pool* pool, const int32_t*
   Plan P;
   if (int r = plan(q, pool, block_table, lengths, scale, shape, workspace, workspace_bytes, nullptr, true, false, &P))
     return r;
-  hipError_t e = kvq::launch_partial(P.a, pool->desc.bits, pool->desc.head_dim, P.qvw, shape->batch,
-                                     static_cast<hipStream_t>(stream));
+  hipError_t e = launch_plan_partial(P, pool, shape->batch, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "partial launch");
   return KVQ_OK;
 }
@@ -369,7 +391,7 @@ int paged_decode_attention(const uint16_t* q, const kvq_pool* pool, const int32_
   if (int r = plan(q, pool, block_table, lengths, scale, shape, workspace, workspace_bytes, out, true, true, &P))
     return r;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = kvq::launch_partial(P.a, pool->desc.bits, pool->desc.head_dim, P.qvw, shape->batch, st);
+  hipError_t e = launch_plan_partial(P, pool, shape->batch, st);
   if (e != hipSuccess) return hip_fail(e, "partial launch");
   e = kvq::launch_merge(P.m, shape->batch, st);
   if (e != hipSuccess) return hip_fail(e, "merge launch");

@@ -71,4 +71,11 @@ hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t stream);
 bool partial_supported(int bits, int D, int qvw);
 int tile_tokens(int bits, int D);
 
+// matrix-core engine (4-bit pages, head dim 128/256, stream schedule, 16 query vectors per wave,
+// 64-token tiles)
+bool mfma_supported(int bits, int D);
+hipError_t launch_partial_mfma(const PartialArgs& a, int D, hipStream_t s);
+constexpr int MFMA_QVW = 16;
+constexpr int MFMA_TILE = 64;
+
 }  // namespace kvq

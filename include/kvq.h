@@ -116,7 +116,19 @@ typedef struct kvq_decode_shape {
   int32_t max_len;             /* host upper bound on every lengths[b] (sizes the grid) */
   int32_t partition_tokens;    /* tokens per split-K partition; 0 = automatic */
   int32_t out_f32;             /* 0: out is bf16; 1: out is f32 (unrounded merge result) */
+  int32_t engine;              /* kvq_engine: which units compute q.k and P.V */
 } kvq_decode_shape;
+
+/* Engines of the partial pass.  Both compute the same quantity to the tolerances stated for
+ * paged_decode_attention.
+ *   KVQ_ENGINE_VECTOR: vector ALU -- v_dot2_f32_bf16 for q.k, f32 FMA for P.V; every format.
+ *   KVQ_ENGINE_MATRIX: matrix cores -- q.k with exact bf16 products, P.V with exact f16 codes
+ *     against the weight split into two f16 halves (~2^-22 relative); 4-bit pages, head_dim
+ *     128 or 256, partition_tokens == 0 only.  It serves the GQA groups where the vector ALU
+ *     rather than HBM bounds the pass ([P50] multi-query.ts puts a KV head's query rows on the
+ *     matrix unit for the same reason).
+ *   KVQ_ENGINE_AUTO: the vector engine. */
+enum kvq_engine { KVQ_ENGINE_AUTO = 0, KVQ_ENGINE_VECTOR = 1, KVQ_ENGINE_MATRIX = 2 };
 
 /* Bytes of workspace paged_decode_attention needs for this shape (0 if the shape is
  * invalid).  The workspace holds per-partition partial outputs (f32). */

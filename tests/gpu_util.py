@@ -45,12 +45,12 @@ def pool_planes_np(pool: kvq.Pool):
     return out
 
 
-def run_decode(w, pool, partition_tokens=0, out_f32=True, q=None, lengths=None, table=None):
+def run_decode(w, pool, partition_tokens=0, out_f32=True, q=None, lengths=None, table=None, engine=0):
     q = u16_dev(w.q_bits) if q is None else q
     table = i32_dev(w.table) if table is None else table
     lengths = i32_dev(w.lengths) if lengths is None else lengths
     out = kvq.decode(q, pool, table, lengths, w.scale, w.max_len, partition_tokens=partition_tokens,
-                     out_f32=out_f32)
+                     out_f32=out_f32, engine=engine)
     torch.cuda.synchronize()
     if out_f32:
         return out.cpu().numpy().astype(np.float64)

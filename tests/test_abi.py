@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_struct_layouts():
     assert ctypes.sizeof(kvq.PoolDesc) == 24
-    assert ctypes.sizeof(kvq.DecodeShape) == 28
+    assert ctypes.sizeof(kvq.DecodeShape) == 32
 
 
 @pytest.mark.parametrize("name,expect", [("c3", 345157632), ("c2", 139984896), ("c1", 1179648),
@@ -89,10 +89,11 @@ class _FakePool:
 @pytest.mark.parametrize("mut,code", [(dict(q_rows=9), -2), (dict(q_rows=0), -2), (dict(num_q_heads=5), -2),
                                       (dict(batch=0), -1), (dict(max_len=0), -1),
                                       (dict(max_blocks_per_seq=1, max_len=1000), -6),
-                                      (dict(partition_tokens=-1), -1)])
+                                      (dict(partition_tokens=-1), -1), (dict(engine=3), -1),
+                                      (dict(engine=2, partition_tokens=64), -2)])
 def test_decode_shape_rejected(lib, mut, code):
     p = _FakePool()
-    s = kvq.DecodeShape(2, 16, 1, 40, 1000, 0, 0)
+    s = kvq.DecodeShape(2, 16, 1, 40, 1000, 0, 0, 0)
     for k, v in mut.items():
         setattr(s, k, v)
     assert lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s)) == 0
@@ -105,7 +106,7 @@ def test_decode_shape_rejected(lib, mut, code):
 
 def test_workspace_too_small_and_null_pointers(lib):
     p = _FakePool()
-    s = kvq.DecodeShape(2, 16, 1, 40, 1000, 256, 0)
+    s = kvq.DecodeShape(2, 16, 1, 40, 1000, 256, 0, 0)
     need = lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s))
     # partials: B*HQ*N*ceil(1000/256) rows of (D + 2) floats (o block padded to 256 B)
     parts = 4
@@ -129,7 +130,7 @@ def test_automatic_schedule_is_the_balanced_stream(lib, monkeypatch):
     workspace holds (waves + units) partial slots of the workgroup's query vectors."""
     monkeypatch.delenv("KVQ_PARTITION_TOKENS", raising=False)
     p = _FakePool()
-    s = kvq.DecodeShape(32, 16, 1, 1100, 32197, 0, 0)
+    s = kvq.DecodeShape(32, 16, 1, 1100, 32197, 0, 0, 0)
     assert lib.paged_decode_partition_tokens(p.handle, ctypes.byref(s)) == 0
     need = lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s))
     waves = 8 * 256                                   # no device here: 256 compute units assumed
@@ -139,3 +140,19 @@ def test_automatic_schedule_is_the_balanced_stream(lib, monkeypatch):
     s.partition_tokens = 300
     assert lib.paged_decode_partition_tokens(p.handle, ctypes.byref(s)) == 300
     p.close()
+
+
+def test_matrix_engine_limits(lib):
+    """The matrix-core engine reads 4-bit pages at head dim 128/256 on the stream schedule; its
+    workspace holds 16 query vectors per slot."""
+    s = kvq.DecodeShape(32, 16, 1, 1100, 32197, 0, 0, 2)
+    for bits, D, ok in [(4, 256, True), (4, 128, True), (8, 256, False), (16, 128, False), (4, 64, False)]:
+        p = _FakePool(bits=bits, D=D)
+        need = lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s))
+        if ok:
+            slots = (8 * 256 + 32 * 2) * 16
+            o = slots * D * 4
+            assert need == ((o + 255) // 256) * 256 + slots * 2 * 4
+        else:
+            assert need == 0
+        p.close()

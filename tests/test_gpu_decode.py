@@ -141,3 +141,58 @@ def test_precondition_violations_do_not_fault_or_leak(filled):
         keep = [0] + list(range(3, w.B))
         G.check_f32(got[keep], ref[keep], tag=f"pt={pt}")
         assert np.all(got[1] == 0)
+
+
+MATRIX = {
+    "c1": dict(),
+    "c3": dict(B=4, len_lo=300, len_hi=2100),
+    "c5": dict(B=3, len_lo=500, len_hi=1500),
+    "c3_d128": dict(B=3, len_lo=100, len_hi=900, D=128, HQ=16, HK=4),
+}
+
+
+@pytest.mark.parametrize("name", list(MATRIX))
+def test_matrix_engine_parity(filled, name):
+    """The matrix-core engine (4-bit pages) against the oracle, to the same tolerances."""
+    kw = dict(MATRIX[name])
+    base = "c3" if name.startswith("c3") else name
+    print(f"matrix {name}", flush=True)
+    w, pool, ref = filled(base, **kw)
+    got = G.run_decode(w, pool, out_f32=True, engine=kvq.ENGINE_MATRIX)
+    G.check_f32(got, ref, tag=f"matrix {name}")
+    bits = G.run_decode(w, pool, out_f32=False, engine=kvq.ENGINE_MATRIX)
+    assert np.array_equal(bits, G.rne_f32_to_bf16(got))
+    G.check_bf16(bits, ref, tag=f"matrix {name}")
+
+
+@pytest.mark.parametrize("case", [
+    dict(name="c5", B=2, len_lo=4, len_hi=4),            # only the N new rows
+    dict(name="c3", B=3, len_lo=1, len_hi=3),            # one to three tokens
+    dict(name="c3", B=2, len_lo=64, len_hi=64),          # exactly one tile
+    dict(name="c3", B=1, len_lo=5000, len_hi=5000, HQ=2, HK=2),        # REP 1
+    dict(name="c5", B=2, len_lo=300, len_hi=700, N=8, HQ=16, HK=2),    # 64 vectors: 4 waves' worth
+    dict(name="c5", B=2, len_lo=300, len_hi=700, N=3, HQ=6, HK=2),     # 9 vectors, padded to 16
+    dict(name="c3", B=3, len_lo=100, len_hi=300, BS=16),              # blocks of 16: tiles span blocks
+])
+def test_matrix_engine_edge_cases(filled, case):
+    case = dict(case)
+    name = case.pop("name")
+    print(f"matrix edge {name} {case}", flush=True)
+    w, pool, ref = filled(name, **case)
+    got = G.run_decode(w, pool, engine=kvq.ENGINE_MATRIX)
+    G.check_f32(got, ref, tag=f"matrix {name} {case}")
+
+
+def test_matrix_engine_poison_and_bad_inputs(filled):
+    w, pool, ref = filled("c3", **SMALL["c3"])
+    clean = G.run_decode(w, pool, engine=kvq.ENGINE_MATRIX)
+    table = w.table.copy()
+    table[0, 0] = w.num_blocks + 1000
+    G.run_decode(w, pool, table=G.i32_dev(table), engine=kvq.ENGINE_MATRIX)
+    lengths = w.lengths.astype(np.int32).copy()
+    lengths[1] = 0
+    lengths[2] = w.max_len + 500
+    got = G.run_decode(w, pool, lengths=G.i32_dev(lengths), engine=kvq.ENGINE_MATRIX)
+    keep = [0] + list(range(3, w.B))
+    assert np.array_equal(got[keep], clean[keep]) or G.check_f32(got[keep], ref[keep]) is not None
+    assert np.all(got[1] == 0)
