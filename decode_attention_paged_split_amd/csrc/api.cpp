@@ -83,10 +83,9 @@ int device_cus() {
 
 constexpr int MAX_PARTS = 8192;
 
-// query vectors per workgroup: the largest power of two <= 8 dividing REP * N (<= 4 for 2-bit
-// pages, whose V lanes hold 16 dims each)
-int qvw_for(int qv, int bits) {
-  for (int w = (bits == 2 ? 4 : 8); w >= 1; w /= 2)
+// query vectors per workgroup: the largest power of two <= kvq::valu_max_qvw dividing REP * N
+int qvw_for(int qv, int bits, int D) {
+  for (int w = kvq::valu_max_qvw(bits, D); w >= 1; w /= 2)
     if (qv % w == 0) return w;
   return 1;
 }
@@ -104,15 +103,25 @@ int choose_partition(const kvq_pool* pool, const kvq_decode_shape* s) {
   return 0;
 }
 
-// waves the stream schedule launches: 8 per compute unit (two per SIMD), all resident at once
-int stream_waves() { return 8 * device_cus(); }
-
 bool use_mfma(const kvq_decode_shape* s) { return s->engine == KVQ_ENGINE_MATRIX; }
+
+// Stream schedule: the most ranges the stream is cut into and the partial slots per (unit, range).
+// Both engines launch 8 waves per compute unit (two per SIMD), all resident at once: the matrix
+// engine gives each wave a range of its own, the vector engine one range per workgroup of 8
+// waves that share its tiles.
+struct StreamGeom {
+  int ranges, sub, min_tokens;
+};
+
+StreamGeom stream_geom(const kvq_decode_shape* s) {
+  if (use_mfma(s)) return {8 * device_cus(), 1, kvq::MFMA_TILE};
+  return {device_cus(), kvq::VALU_STREAM_WAVES, kvq::VALU_STREAM_WAVES * kvq::VALU_TILE};
+}
 
 // query vectors per workgroup (vector ALU) or per wave (matrix cores, padded to 16)
 int qvw_of(const kvq_pool* pool, const kvq_decode_shape* s) {
   const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
-  return use_mfma(s) ? kvq::MFMA_QVW : qvw_for(qv, pool->desc.bits);
+  return use_mfma(s) ? kvq::MFMA_QVW : qvw_for(qv, pool->desc.bits, pool->desc.head_dim);
 }
 
 int qgroups_of(const kvq_pool* pool, const kvq_decode_shape* s) {
@@ -153,28 +162,40 @@ int validate_shape(const kvq_pool* pool, const kvq_decode_shape* s) {
     if (pt > 0)
       return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core engine runs the balanced stream schedule only "
                                        "(partition_tokens = 0)");
-  } else if (!kvq::partial_supported(pool->desc.bits, pool->desc.head_dim, qvw_for(qv, pool->desc.bits))) {
+  } else if (!kvq::partial_supported(pool->desc.bits, pool->desc.head_dim, qvw_for(qv, pool->desc.bits, pool->desc.head_dim))) {
     return fail(KVQ_ERR_UNSUPPORTED, "no kernel for bits=%d D=%d", pool->desc.bits, pool->desc.head_dim);
   }
   return KVQ_OK;
 }
 
 // Partials: fixed partitions hold [B, HQ, N, parts] rows; the stream schedule holds
-// (waves + units) slots of QVW vectors (slot = unit + wave).  Each partial row is D floats of
-// unnormalised output plus (max, normaliser).
-size_t workspace_layout(const kvq_pool* pool, const kvq_decode_shape* s, int pt, size_t* ml_off) {
+// (ranges + units) * sub slots of QVW vectors (slot = (unit + range) * sub + wave in range).  Each partial row is D floats of
+// unnormalised output plus (max, normaliser).  The vector engine adds its copy of q in the
+// codes' pair order, [units, D/64, QVW] blocks of q_block_words words.
+struct WsLayout {
+  size_t ml_off, qp_off, total;
+};
+
+WsLayout workspace_layout(const kvq_pool* pool, const kvq_decode_shape* s, int pt) {
   size_t rows;
   if (pt > 0) {
     const size_t parts = (size_t)(s->max_len + pt - 1) / pt;
     rows = (size_t)s->batch * s->num_q_heads * s->q_rows * parts;
   } else {
     const size_t units = (size_t)s->batch * pool->desc.num_kv_heads * qgroups_of(pool, s);
-    rows = ((size_t)stream_waves() + units) * qvw_of(pool, s);
+    const StreamGeom sg = stream_geom(s);
+    rows = ((size_t)sg.ranges + units) * sg.sub * qvw_of(pool, s);
   }
-  size_t o_bytes = rows * pool->desc.head_dim * sizeof(float);
-  o_bytes = (o_bytes + 255) & ~(size_t)255;
-  *ml_off = o_bytes;
-  return o_bytes + rows * 2 * sizeof(float);
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  WsLayout L{};
+  L.ml_off = up(rows * pool->desc.head_dim * sizeof(float));
+  L.qp_off = L.total = L.ml_off + rows * 2 * sizeof(float);
+  if (!use_mfma(s)) {
+    const size_t qv = (size_t)s->batch * pool->desc.num_kv_heads * qgroups_of(pool, s) * qvw_of(pool, s);
+    L.qp_off = up(L.total);
+    L.total = L.qp_off + qv * (pool->desc.head_dim / 64) * kvq::q_block_words(pool->desc.bits != 16) * 4;
+  }
+  return L;
 }
 
 }  // namespace
@@ -286,8 +307,7 @@ int kv_append_quantize(kvq_pool* pool, const uint16_t* k, const uint16_t* v, con
 
 size_t paged_decode_workspace_bytes(const kvq_pool* pool, const kvq_decode_shape* shape) {
   if (validate_shape(pool, shape) != KVQ_OK) return 0;
-  size_t ml_off = 0;
-  return workspace_layout(pool, shape, choose_partition(pool, shape), &ml_off);
+  return workspace_layout(pool, shape, choose_partition(pool, shape)).total;
 }
 
 int32_t paged_decode_partition_tokens(const kvq_pool* pool, const kvq_decode_shape* shape) {
@@ -319,8 +339,8 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
       !aligned(workspace, 16) || (need_out && !aligned(out, shape->out_f32 ? 4 : 2)))
     return fail(KVQ_ERR_INVALID, "misaligned pointer (q and workspace need 16 bytes)");
   const int pt = choose_partition(pool, shape);
-  size_t ml_off = 0;
-  const size_t need = workspace_layout(pool, shape, pt, &ml_off);
+  const WsLayout L = workspace_layout(pool, shape, pt);
+  const size_t need = L.total;
   if (workspace_bytes < need)
     return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   const kvq_pool_desc& d = pool->desc;
@@ -338,7 +358,8 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   a.vb = static_cast<const uint16_t*>(pool->planes[KVQ_PLANE_V_BIAS]);
   a.table = block_table; a.lengths = lengths;
   a.opart = static_cast<float*>(workspace);
-  a.ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_off);
+  a.ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_off);
+  a.qp = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + L.qp_off);
   a.scale_log2e = scale * 1.4426950408889634f;
   a.HQ = shape->num_q_heads; a.HK = d.num_kv_heads; a.N = shape->q_rows; a.BS = d.block_size;
   a.bs_shift = -1;
@@ -347,7 +368,8 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   a.max_blocks = shape->max_blocks_per_seq; a.num_blocks = d.num_blocks; a.max_len = shape->max_len;
   a.part_tokens = pt; a.num_parts = parts; a.qgroups = qgroups_of(pool, shape);
   a.len_cap = (int)std::min<long>(shape->max_len, (long)shape->max_blocks_per_seq * d.block_size);
-  a.batch = shape->batch; a.num_waves = stream_waves(); a.min_tokens = P->mfma ? kvq::MFMA_TILE : kvq::tile_tokens(d.bits, d.head_dim);
+  const StreamGeom sg = stream_geom(shape);
+  a.batch = shape->batch; a.num_ranges = sg.ranges; a.range_sub = sg.sub; a.min_tokens = sg.min_tokens;
 
   kvq::MergeArgs& m = P->m;
   m = kvq::MergeArgs{};
@@ -356,7 +378,7 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   m.num_parts = parts; m.out_f32 = shape->out_f32 ? 1 : 0; m.max_len = shape->max_len;
   m.len_cap = a.len_cap;
   m.batch = shape->batch; m.HK = d.num_kv_heads; m.qgroups = a.qgroups; m.qvw = P->qvw;
-  m.num_waves = a.num_waves; m.min_tokens = a.min_tokens;
+  m.num_ranges = a.num_ranges; m.range_sub = a.range_sub; m.min_tokens = a.min_tokens;
   return KVQ_OK;
 }
 

@@ -41,14 +41,16 @@ struct PartialArgs {
   const int32_t* lengths;   // [B]
   float* opart;             // [B, HQ, N, P, D] f32, unnormalised
   float* ml;                // [B, HQ, N, P, 2] f32: running max (log2 units), normaliser
+  uint32_t* qp;             // vector engine: [units, D/64, QVW, q_block_words] q in the codes' order
   float scale_log2e;        // softmax scale * log2(e)
   int32_t HQ, HK, N, BS, bs_shift, max_blocks, num_blocks, max_len;
   int32_t part_tokens;      // > 0: fixed partitions of this many tokens; 0: balanced stream
   int32_t num_parts;        // fixed partitions: partitions per sequence (grid x)
   int32_t qgroups;          // query groups of QVW vectors per KV head
   int32_t batch;
-  int32_t num_waves;        // stream: waves launched
-  int32_t min_tokens;       // stream: fewest tokens per working wave (one tile)
+  int32_t num_ranges;       // stream: most ranges the stream is cut into (one per workgroup or wave)
+  int32_t range_sub;        // stream: partial slots per (unit, range): the waves sharing a range
+  int32_t min_tokens;       // stream: fewest tokens per working range
   int32_t len_cap;          // min(max_len, max_blocks * BS): lengths are clamped to [0, len_cap]
 };
 
@@ -59,8 +61,12 @@ struct MergeArgs {
   void* out;                // [B, HQ, N, D] bf16 or f32
   int32_t HQ, N, D, part_tokens, num_parts, out_f32, max_len;
   int32_t len_cap;          // min(max_len, max_blocks * BS): lengths are clamped to [0, len_cap]
-  int32_t batch, HK, qgroups, qvw, num_waves, min_tokens;   // stream schedule (part_tokens == 0)
+  int32_t batch, HK, qgroups, qvw, num_ranges, range_sub, min_tokens;   // stream (part_tokens == 0)
 };
+
+// words per (scale group, query vector) block of the vector engine's q copy: 32 bf16 pairs,
+// then (affine pages) the f32 sum of q over the group
+constexpr int q_block_words(bool affine) { return affine ? 36 : 32; }
 
 hipError_t launch_append(const AppendArgs& a, int bits, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
@@ -69,7 +75,9 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_partial(const PartialArgs& a, int bits, int D, int qvw, int B, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t stream);
 bool partial_supported(int bits, int D, int qvw);
-int tile_tokens(int bits, int D);
+// most query vectors one wave of the vector engine carries: 8, or 4 where a V lane owns 16 head
+// dims (2-bit pages; bf16 and 8-bit pages at head dim 256)
+constexpr int valu_max_qvw(int bits, int D) { return (bits == 2 || (D == 256 && bits >= 8)) ? 4 : 8; }
 
 // matrix-core engine (4-bit pages, head dim 128/256, stream schedule, 16 query vectors per wave,
 // 64-token tiles)
@@ -77,5 +85,9 @@ bool mfma_supported(int bits, int D);
 hipError_t launch_partial_mfma(const PartialArgs& a, int D, hipStream_t s);
 constexpr int MFMA_QVW = 16;
 constexpr int MFMA_TILE = 64;
+// vector engine, stream schedule: one workgroup of VALU_STREAM_WAVES waves per compute unit owns
+// a range and shares its 64-token tiles among its waves
+constexpr int VALU_STREAM_WAVES = 8;
+constexpr int VALU_TILE = 64;
 
 }  // namespace kvq

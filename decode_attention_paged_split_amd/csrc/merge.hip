@@ -6,9 +6,15 @@
 // M = max_p m_p; partitions whose max is -inf (no visible token) are skipped.  Maxima are in
 // log2 units here (the partial kernel scales scores by log2(e)), so the weights are exp2.
 // One workgroup per output row: the partition weights are computed once into LDS, then each
-// thread accumulates one head dim.  Output is bf16 (round to nearest even) or f32.
+// thread accumulates four head dims over a stride of the partials (several loads in flight per
+// thread) and the strides' sums are added in LDS.  Output is bf16 (round to nearest even) or f32.
+// Stream schedule: the stream of T tokens is cut into R = min(num_ranges, ceil(T / min_tokens))
+// ranges; a unit's partials sit in range_sub consecutive slots per range it meets, from slot
+// (unit + first range) * range_sub on.
 #include "device_common.hpp"
 #include "kernels.hpp"
+
+#include <algorithm>
 
 namespace kvq {
 
@@ -51,7 +57,7 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     for (int w = 0; w < nw; ++w) { pre += red64[0][w]; tot += red64[1][w]; }
     const int HQG = a.HK * a.qgroups;
     const int64_t T = (int64_t)tot * HQG;
-    const int64_t weff = min<int64_t>((int64_t)a.num_waves, (T + a.min_tokens - 1) / a.min_tokens);
+    const int64_t weff = min<int64_t>((int64_t)a.num_ranges, (T + a.min_tokens - 1) / a.min_tokens);
     const int REP = a.HQ / a.HK;
     const int hk = h / REP;
     const int jj = (h - hk * REP) * a.N + i;
@@ -61,8 +67,8 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
       const int64_t start = (int64_t)pre * HQG + (int64_t)(hk * a.qgroups + qg) * len;
       const int64_t end = start + len;
       const int64_t w_first = start * weff / T, w_last = (end - 1) * weff / T;
-      nparts = (int)(w_last - w_first + 1);
-      const int64_t slot0 = u + w_first;
+      nparts = (int)(w_last - w_first + 1) * a.range_sub;
+      const int64_t slot0 = (u + w_first) * a.range_sub;
       mbase = (slot0 * a.qvw + j) * 2;
       obase = (slot0 * a.qvw + j) * a.D;
       mstride = (int64_t)a.qvw * 2;
@@ -92,19 +98,48 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   float tot = 0.0f;
   for (int w = 0; w < nw; ++w) tot += red[w];
 
-  for (int d = tid; d < a.D; d += blockDim.x) {
-    float num = 0.0f;
-    for (int p = 0; p < nparts; ++p) num = fmaf(sw[p], a.opart[obase + p * ostride + d], num);
-    const float r = (tot > 0.0f) ? num / tot : 0.0f;
-    if (a.out_f32) static_cast<float*>(a.out)[(int64_t)row * a.D + d] = r;
-    else static_cast<uint16_t*>(a.out)[(int64_t)row * a.D + d] = (uint16_t)f32_to_bf16_rne(r);
+  // weighted sum of the partials: thread (stream s, dim lane dl) owns dims 4 dl .. 4 dl + 3 and
+  // partials s, s + S, ...; the S streams' sums are added in LDS
+  const int DL = a.D / 4, S = blockDim.x / DL;
+  const int dl = tid % DL, sidx = tid / DL;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (sidx < S) {
+    const float* ob = a.opart + obase + 4 * dl;
+#pragma unroll 4
+    for (int p = sidx; p < nparts; p += S) {
+      const float wp = sw[p];
+      if (wp != 0.0f) {                                  // (a skipped partial's o is never read)
+        const float4 o = *reinterpret_cast<const float4*>(ob + p * ostride);
+        acc.x = fmaf(wp, o.x, acc.x); acc.y = fmaf(wp, o.y, acc.y);
+        acc.z = fmaf(wp, o.z, acc.z); acc.w = fmaf(wp, o.w, acc.w);
+      }
+    }
+  }
+  __syncthreads();                                       // sw is reused for the stream sums
+  float4* part = reinterpret_cast<float4*>(sw);
+  if (sidx < S) part[sidx * DL + dl] = acc;
+  __syncthreads();
+  if (tid < DL) {
+    float4 r = part[tid];
+    for (int k = 1; k < S; ++k) {
+      const float4 x = part[k * DL + tid];
+      r.x += x.x; r.y += x.y; r.z += x.z; r.w += x.w;
+    }
+    const float v[4] = {r.x, r.y, r.z, r.w};
+    for (int k = 0; k < 4; ++k) {
+      const float y = (tot > 0.0f) ? v[k] / tot : 0.0f;
+      const int64_t oi = (int64_t)row * a.D + 4 * tid + k;
+      if (a.out_f32) static_cast<float*>(a.out)[oi] = y;
+      else static_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_rne(y);
+    }
   }
 }
 
 hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t s) {
   const unsigned rows = (unsigned)(B * a.HQ * a.N);
-  const int most = a.part_tokens > 0 ? a.num_parts : a.num_waves + 1;
-  const size_t shm = (size_t)most * sizeof(float);
+  const int most = a.part_tokens > 0 ? a.num_parts : (a.num_ranges + 1) * a.range_sub;
+  // partition weights, then the 256 threads' float4 sums
+  const size_t shm = (size_t)std::max(most, 256 * 4) * sizeof(float);
   hipLaunchKernelGGL(merge_kernel, dim3(rows), dim3(256), shm, s, a);
   return hipGetLastError();
 }

@@ -129,7 +129,7 @@ __global__ void __launch_bounds__(MF_WAVES * 64, 1)
 partial_mfma_kernel(PartialArgs a) {
   using Mg = MGeo<D>;
   constexpr int G = Mg::G, KSTEPS = Mg::KSTEPS, KSETS = Mg::KSETS, DT = Mg::DT, ROWB = Mg::ROWB;
-  constexpr int CPR = Mg::CPR, NVL = Mg::NVL, PITCH = Mg::PITCH;
+  constexpr int CPR = Mg::CPR, NVL = Mg::NVL;
   __shared__ __align__(16) MScratch<D> scr[MF_WAVES];
 
   const int lane = threadIdx.x & 63;
@@ -149,7 +149,7 @@ partial_mfma_kernel(PartialArgs a) {
     tot += s;
   }
   const int64_t T = mf_uni64(tot) * HQG;
-  const int W_eff = (int)min<int64_t>((int64_t)a.num_waves, (T + a.min_tokens - 1) / a.min_tokens);
+  const int W_eff = (int)min<int64_t>((int64_t)a.num_ranges, (T + a.min_tokens - 1) / a.min_tokens);
   if (w >= W_eff) return;                          // no block-level barriers in this kernel
   const int64_t x0 = ((int64_t)w * T + W_eff - 1) / W_eff;
   const int64_t x1 = ((int64_t)(w + 1) * T + W_eff - 1) / W_eff;
@@ -435,7 +435,7 @@ partial_mfma_kernel(PartialArgs a) {
 bool mfma_supported(int bits, int D) { return bits == 4 && (D == 128 || D == 256); }
 
 hipError_t launch_partial_mfma(const PartialArgs& a, int D, hipStream_t s) {
-  dim3 grid((unsigned)(a.num_waves / MF_WAVES));
+  dim3 grid((unsigned)(a.num_ranges / MF_WAVES));
   switch (D) {
     case 128: hipLaunchKernelGGL(partial_mfma_kernel<128>, grid, dim3(MF_WAVES * 64), 0, s, a); break;
     case 256: hipLaunchKernelGGL(partial_mfma_kernel<256>, grid, dim3(MF_WAVES * 64), 0, s, a); break;

@@ -104,14 +104,26 @@ def test_decode_shape_rejected(lib, mut, code):
     p.close()
 
 
+def _up(x):
+    return (x + 255) // 256 * 256
+
+
+def _ws_bytes(rows, D, qvecs=0, affine=True):
+    """partials: rows of D floats (padded to 256 B) + rows of (max, normaliser); then the vector
+    engine's q copy (per query vector and 64-dim group a block of 36 words, 32 on bf16 pages)"""
+    total = _up(rows * D * 4) + rows * 2 * 4
+    if qvecs:
+        total = _up(total) + qvecs * (D // 64) * (36 if affine else 32) * 4
+    return total
+
+
 def test_workspace_too_small_and_null_pointers(lib):
     p = _FakePool()
     s = kvq.DecodeShape(2, 16, 1, 40, 1000, 256, 0, 0)
     need = lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s))
-    # partials: B*HQ*N*ceil(1000/256) rows of (D + 2) floats (o block padded to 256 B)
+    # partials: B*HQ*N*ceil(1000/256) rows; q copy: B*HQ*N query vectors
     parts = 4
-    o = 2 * 16 * parts * 256 * 4
-    assert need == ((o + 255) // 256) * 256 + 2 * 16 * parts * 2 * 4
+    assert need == _ws_bytes(2 * 16 * parts, 256, qvecs=2 * 16)
     rc = lib.paged_decode_attention(ctypes.c_void_p(256), p.handle, ctypes.c_void_p(256), ctypes.c_void_p(256),
                                     1.0, ctypes.byref(s), ctypes.c_void_p(256), need - 1, ctypes.c_void_p(256),
                                     None)
@@ -127,16 +139,16 @@ def test_workspace_too_small_and_null_pointers(lib):
 
 def test_automatic_schedule_is_the_balanced_stream(lib, monkeypatch):
     """partition_tokens == 0 selects the balanced stream schedule (reported as 0 tokens); its
-    workspace holds (waves + units) partial slots of the workgroup's query vectors."""
+    workspace holds (ranges + units) * 8 partial slots of a wave's query vectors (one range per
+    workgroup of 8 waves)."""
     monkeypatch.delenv("KVQ_PARTITION_TOKENS", raising=False)
     p = _FakePool()
     s = kvq.DecodeShape(32, 16, 1, 1100, 32197, 0, 0, 0)
     assert lib.paged_decode_partition_tokens(p.handle, ctypes.byref(s)) == 0
     need = lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s))
-    waves = 8 * 256                                   # no device here: 256 compute units assumed
-    slots = (waves + 32 * 2) * 8                      # units = B * HK (one query group of 8)
-    o = slots * 256 * 4
-    assert need == ((o + 255) // 256) * 256 + slots * 2 * 4
+    ranges = 256                                      # no device here: 256 compute units assumed
+    slots = (ranges + 32 * 2) * 8 * 8                 # units = B * HK (one query group of 8),
+    assert need == _ws_bytes(slots, 256, qvecs=32 * 16)   # 8 waves per range, 8 vectors
     s.partition_tokens = 300
     assert lib.paged_decode_partition_tokens(p.handle, ctypes.byref(s)) == 300
     p.close()
@@ -151,8 +163,7 @@ def test_matrix_engine_limits(lib):
         need = lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s))
         if ok:
             slots = (8 * 256 + 32 * 2) * 16
-            o = slots * D * 4
-            assert need == ((o + 255) // 256) * 256 + slots * 2 * 4
+            assert need == _ws_bytes(slots, D)
         else:
             assert need == 0
         p.close()

@@ -1,10 +1,16 @@
 """GPU: paged decode attention (partial + merge) against the f64 oracle.
 
 Tolerances: the f32 output (out_f32=1) is within max abs 2e-3 and relative L2 2e-3 of the
-oracle; the bf16 output is exactly the round-to-nearest-even of the f32 output, and within
-rel L2 2e-3 / max abs max(2e-3, one bf16 ulp of the reference) of the oracle.  The shapes
-below are the workloads' own shapes at reduced batch and length (several partitions and a
-ragged tail), plus edge cases."""
+oracle; the bf16 output is the round-to-nearest-even of the f32 output, and within rel L2 2e-3 /
+max abs max(2e-3, one bf16 ulp of the reference) of the oracle.  The shapes below are the
+workloads' own shapes at reduced batch and length (several partitions and a ragged tail), plus
+edge cases.
+
+Fixed partitions (partition_tokens > 0) and the matrix engine are bit-for-bit deterministic.
+The vector engine's stream schedule shares each range's tiles among its waves at run time, so
+which wave sums which tiles varies from call to call: its results agree to f32 rounding
+(checked below), and a bf16 output may differ by one unit in the last place from the rounding
+of another call's f32 output."""
 import numpy as np
 import pytest
 import torch
@@ -51,7 +57,12 @@ def test_decode_parity(filled, name, pt):
     got = G.run_decode(w, pool, partition_tokens=pt, out_f32=True)
     G.check_f32(got, ref, tag=f"{name} pt={pt}")
     bits = G.run_decode(w, pool, partition_tokens=pt, out_f32=False)
-    assert np.array_equal(bits, G.rne_f32_to_bf16(got)), "bf16 output must be RNE of the f32 output"
+    rne = G.rne_f32_to_bf16(got)
+    if pt > 0:
+        assert np.array_equal(bits, rne), "bf16 output must be RNE of the f32 output"
+    else:                           # one bf16 ulp (2^-7 relative at most), or a sign flip at ~0
+        b, r = G.bf16_to_f64(bits), G.bf16_to_f64(rne)
+        assert np.all(np.abs(b - r) <= 2.0 ** -7 * np.abs(r) + 1e-6)
     G.check_bf16(bits, ref, tag=f"{name} pt={pt}")
 
 
@@ -65,10 +76,14 @@ def test_partition_count_invariance(filled):
 
 
 def test_deterministic(filled):
+    """Fixed partitions repeat bit for bit; the stream schedule repeats to f32 rounding."""
     w, pool, _ = filled("c3", **SMALL["c3"])
+    a = G.run_decode(w, pool, partition_tokens=64)
+    b = G.run_decode(w, pool, partition_tokens=64)
+    assert np.array_equal(a, b)
     a = G.run_decode(w, pool)
     b = G.run_decode(w, pool)
-    assert np.array_equal(a, b)
+    assert np.abs(a - b).max() <= 1e-6 * np.abs(a).max()
 
 
 @pytest.mark.parametrize("case", [
@@ -114,7 +129,8 @@ def test_poisoned_tail_and_free_blocks_are_not_read(filled, name):
     for n in names:
         pp.planes[n].masked_fill_(mask[..., None].expand_as(pp.planes[n]), nan_bf16)
     got = G.run_decode(w, pp)
-    assert np.array_equal(got, clean)
+    assert np.all(np.isfinite(got))
+    assert np.abs(got - clean).max() <= 1e-6 * np.abs(clean).max()
     pp.close()
 
 
