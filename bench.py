@@ -39,8 +39,10 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources that decide what the partial kernel reads and writes (its code and the
+    host-side launch geometry)."""
     h = hashlib.sha256()
-    for f in ("partial_valu.hip", "device_common.hpp", "kernels.hpp"):
+    for f in ("partial_valu.hip", "device_common.hpp", "kernels.hpp", "api.cpp"):
         with open(os.path.join(ROOT, "decode_attention_paged_split_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -182,16 +184,16 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] setup {time.time() - t_setup:.0f} s; partition {pt} tokens; workspace {ws.numel() >> 20} MiB")
 
-    def step(ev=None):
+    def step(ev=None, shp=shape, wsp=ws):
         if ev is not None:
             ev[0].record()
         kvq.kv_append_quantize(pool, nk, nv, ns)
         if ev is not None:
             ev[1].record()
-        kvq.paged_decode_partial(q, pool, table, lengths, w.scale, shape, ws)
+        kvq.paged_decode_partial(q, pool, table, lengths, w.scale, shp, wsp)
         if ev is not None:
             ev[2].record()
-        kvq.paged_decode_merge(pool, lengths, shape, ws, out)
+        kvq.paged_decode_merge(pool, lengths, shp, wsp, out)
         if ev is not None:
             ev[3].record()
 
@@ -223,12 +225,33 @@ def main():
     gbs = eff / (ms_step * 1e-3) / 1e9
     part_s = float(np.mean(par)) * 1e-3
     achieved = eff / part_s / 1e9
-    src_hash = kernel_source_hash()
+    src_hash = kernel_source_hash() if args.engine != "matrix" else None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profiles(w.name, src_hash),
-            "kernel": "partial_kernel", "kernel_us": round(part_s * 1e6, 2),
+            "traffic": traffic_from_profiles(w.name, src_hash) if src_hash else None,
+            "kernel": "partial pass (q copy + partial kernel, events around paged_decode_partial)",
+            "kernel_us": round(part_s * 1e6, 2),
             "algorithmic_bytes_per_launch": eff, "kernel_source_hash": src_hash}
+
+    variants = {}
+    if args.engine == "auto" and w.bits == 4 and w.D in (128, 256) and args.partition_tokens == 0:
+        # the separately flagged matrix-core engine on the same inputs, timed the same way
+        shp_m = kvq.make_shape(pool, w.B, w.HQ, w.N, w.max_blocks, w.max_len, 0, False, kvq.ENGINE_MATRIX)
+        ws_m = torch.empty(kvq.paged_decode_workspace_bytes(pool, shp_m), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            step(None, shp_m, ws_m)
+        evm = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(evm[i], shp_m, ws_m)
+        torch.cuda.synchronize()
+        ms_m = evm[0][0].elapsed_time(evm[-1][3]) / args.steps
+        par_m = float(np.mean([e[1].elapsed_time(e[2]) for e in evm]))
+        variants["matrix_engine"] = {
+            "value": round(eff / (ms_m * 1e-3) / 1e9, 1), "unit": "GB/s", "us_per_step": round(ms_m * 1e3, 2),
+            "partial_us": round(par_m * 1e3, 2), "partial_frac_hbm": round(eff / (par_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "engine=2: MFMA q.k and P.V, 4-bit pages; not the default path"}
+        log(f"[bench] matrix engine: {ms_m * 1e3:.1f} us/step (partial {par_m * 1e3:.1f})")
     rec = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
@@ -244,6 +267,8 @@ def main():
                        "merge": round(float(np.mean(mer)) * 1e3, 2)},
         "roofline": roof,
     }
+    if variants:
+        rec["variants"] = variants
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
