@@ -1,10 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark: one paged decode step of 4-bit, group-64 affine KV pages at head dim 256.
 
-A step is the whole hot path on one batch: quantize-on-append of the B*N new K/V rows into
-their pool slots, the split-K partial kernel over every cached token (block-table reads,
-dequantize-on-load, GQA-shared K/V rows, online softmax in f32), and the log-sum-exp merge.
-Inputs are seeded synthetic data resident in HBM before timing starts.
+A step is the whole hot path on one batch, run through the library's decode-step entry points
+(paged_decode_step_partial, then paged_decode_merge): quantize-on-append of the B*N new K/V rows
+into the slots their positions take in the block table, the copy of q in the codes' order, the
+split-K partial kernel over every cached token (block-table reads, dequantize-on-load,
+GQA-shared K/V rows, online softmax in f32), and the log-sum-exp merge.  Inputs are seeded
+synthetic data resident in HBM before timing starts; the pool holds every cached row but each
+sequence's last N, which every step appends again (same rows, same slots).
 
 Default workload ("c3"): 32 sequences with lengths drawn uniformly in [4096, 32768] tokens
 (sum 598,835), block size 32 with a shuffled block table, 16 query heads over 2 KV heads
@@ -184,18 +187,16 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] setup {time.time() - t_setup:.0f} s; partition {pt} tokens; workspace {ws.numel() >> 20} MiB")
 
-    def step(ev=None, shp=shape, wsp=ws):
-        if ev is not None:
-            ev[0].record()
-        kvq.kv_append_quantize(pool, nk, nv, ns)
-        if ev is not None:
-            ev[1].record()
-        kvq.paged_decode_partial(q, pool, table, lengths, w.scale, shp, wsp)
-        if ev is not None:
-            ev[2].record()
+    kn = nk.view(w.B, w.N, w.HK, w.D)
+    vn = nv.view(w.B, w.N, w.HK, w.D)
+
+    def step(mid=None, shp=shape, wsp=ws):
+        """one decode step: paged_decode_step_partial (append of the new rows with slots from the
+        block table, q copy, partial kernel), then paged_decode_merge"""
+        kvq.paged_decode_step_partial(q, kn, vn, pool, table, lengths, w.scale, shp, wsp)
+        if mid is not None:
+            mid.record()
         kvq.paged_decode_merge(pool, lengths, shp, wsp, out)
-        if ev is not None:
-            ev[3].record()
 
     for _ in range(args.warmup):
         if flush is not None:
@@ -204,22 +205,31 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # two events per step: after the partial pass and after the merge (the previous step's end,
+    # or the start event, opens the next step)
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev0 = E()
+    mids = [E() for _ in range(args.steps)]
+    ends = [E() for _ in range(args.steps)]
+    starts = [E() for _ in range(args.steps)] if flush is not None else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     for i in range(args.steps):
         if flush is not None:
             flush.fill_(1)
-        step(evs[i])
+            starts[i].record()
+        step(mids[i])
+        ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    app = [e[0].elapsed_time(e[1]) for e in evs]
-    par = [e[1].elapsed_time(e[2]) for e in evs]
-    mer = [e[2].elapsed_time(e[3]) for e in evs]
-    tot = [e[0].elapsed_time(e[3]) for e in evs]
-    ms_step = float(np.mean(tot)) if args.cold else evs[0][0].elapsed_time(evs[-1][3]) / args.steps
-    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (append {np.mean(app) * 1e3:.1f}, "
-        f"partial {np.mean(par) * 1e3:.1f}, merge {np.mean(mer) * 1e3:.1f}); wall {wall:.3f} s")
+    opens = starts if starts is not None else [ev0] + ends[:-1]
+    par = [o.elapsed_time(m) for o, m in zip(opens, mids)]
+    mer = [m.elapsed_time(e) for m, e in zip(mids, ends)]
+    tot = [o.elapsed_time(e) for o, e in zip(opens, ends)]
+    ms_step = float(np.mean(tot)) if args.cold else ev0.elapsed_time(ends[-1]) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (append + q copy + partial "
+        f"{np.mean(par) * 1e3:.1f}, merge {np.mean(mer) * 1e3:.1f}); wall {wall:.3f} s")
 
     eff = w.effective_bytes()
     gbs = eff / (ms_step * 1e-3) / 1e9
@@ -229,7 +239,8 @@ def main():
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profiles(w.name, src_hash) if src_hash else None,
-            "kernel": "partial pass (q copy + partial kernel, events around paged_decode_partial)",
+            "kernel": "partial pass: append of the step's rows + q copy + partial kernel "
+                      "(events around paged_decode_step_partial)",
             "kernel_us": round(part_s * 1e6, 2),
             "algorithmic_bytes_per_launch": eff, "kernel_source_hash": src_hash}
 
@@ -240,13 +251,17 @@ def main():
         ws_m = torch.empty(kvq.paged_decode_workspace_bytes(pool, shp_m), dtype=torch.uint8, device=dev)
         for _ in range(3):
             step(None, shp_m, ws_m)
-        evm = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        e0m = E()
+        midm = [E() for _ in range(args.steps)]
+        endm = [E() for _ in range(args.steps)]
         torch.cuda.synchronize()
+        e0m.record()
         for i in range(args.steps):
-            step(evm[i], shp_m, ws_m)
+            step(midm[i], shp_m, ws_m)
+            endm[i].record()
         torch.cuda.synchronize()
-        ms_m = evm[0][0].elapsed_time(evm[-1][3]) / args.steps
-        par_m = float(np.mean([e[1].elapsed_time(e[2]) for e in evm]))
+        ms_m = e0m.elapsed_time(endm[-1]) / args.steps
+        par_m = float(np.mean([o.elapsed_time(m) for o, m in zip([e0m] + endm[:-1], midm)]))
         variants["matrix_engine"] = {
             "value": round(eff / (ms_m * 1e-3) / 1e9, 1), "unit": "GB/s", "us_per_step": round(ms_m * 1e3, 2),
             "partial_us": round(par_m * 1e3, 2), "partial_frac_hbm": round(eff / (par_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -263,8 +278,7 @@ def main():
                    "partition_tokens": pt, "cold": bool(args.cold), "engine": args.engine},
         "us_per_step": round(ms_step * 1e3, 2), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "effective_bytes": eff,
-        "kernels_us": {"append": round(float(np.mean(app)) * 1e3, 2), "partial": round(part_s * 1e6, 2),
-                       "merge": round(float(np.mean(mer)) * 1e3, 2)},
+        "kernels_us": {"append_qcopy_partial": round(part_s * 1e6, 2), "merge": round(float(np.mean(mer)) * 1e3, 2)},
         "roofline": roof,
     }
     if variants:

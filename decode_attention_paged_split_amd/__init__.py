@@ -27,7 +27,8 @@ __all__ = [
     "KvqError", "PoolDesc", "DecodeShape", "Pool", "decode", "lib", "kv_pool_create", "kv_pool_wrap",
     "kv_pool_destroy", "kv_pool_plane_bytes", "kv_append_quantize", "paged_decode_workspace_bytes",
     "paged_decode_partition_tokens", "paged_decode_attention", "paged_decode_partial",
-    "paged_decode_merge", "kv_gather_debug", "make_shape", "gather", "PLANES", "LIB_PATH",
+    "paged_decode_merge", "paged_decode_step", "paged_decode_step_partial", "kv_gather_debug", "make_shape", "gather", "decode_step",
+    "PLANES", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
@@ -92,6 +93,10 @@ def lib() -> ctypes.CDLL:
                                                     _P, ctypes.c_size_t, _P]),
             "paged_decode_merge": (ctypes.c_int, [_P, _P, ctypes.POINTER(DecodeShape), _P, ctypes.c_size_t,
                                                   _P, _P]),
+            "paged_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                                 ctypes.POINTER(DecodeShape), _P, ctypes.c_size_t, _P, _P]),
+            "paged_decode_step_partial": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                                         ctypes.POINTER(DecodeShape), _P, ctypes.c_size_t, _P]),
             "kv_gather_debug": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                _P * 6, _P]),
         }
@@ -173,6 +178,24 @@ def paged_decode_attention(q, pool: "Pool", block_table, lengths, scale: float, 
     _check(lib().paged_decode_attention(_ptr(q), pool.handle, _ptr(block_table), _ptr(lengths),
                                         float(scale), ctypes.byref(shape), _ptr(workspace), ws_bytes,
                                         _ptr(out), _stream(stream)))
+
+
+def paged_decode_step(q, k_new, v_new, pool: "Pool", block_table, lengths, scale: float, shape: DecodeShape,
+                      workspace, out, stream=None) -> None:
+    _need_cuda(q, k_new, v_new, block_table, lengths, workspace, out)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().paged_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), pool.handle, _ptr(block_table),
+                                   _ptr(lengths), float(scale), ctypes.byref(shape), _ptr(workspace), ws_bytes,
+                                   _ptr(out), _stream(stream)))
+
+
+def paged_decode_step_partial(q, k_new, v_new, pool: "Pool", block_table, lengths, scale: float,
+                              shape: DecodeShape, workspace, stream=None) -> None:
+    _need_cuda(q, k_new, v_new, block_table, lengths, workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().paged_decode_step_partial(_ptr(q), _ptr(k_new), _ptr(v_new), pool.handle, _ptr(block_table),
+                                           _ptr(lengths), float(scale), ctypes.byref(shape), _ptr(workspace),
+                                           ws_bytes, _stream(stream)))
 
 
 def paged_decode_partial(q, pool: "Pool", block_table, lengths, scale: float, shape: DecodeShape,
@@ -273,6 +296,25 @@ def decode(q, pool: Pool, block_table, lengths, scale: float, max_len: int, part
         out = torch.empty((B, HQ, N, D), dtype=torch.float32 if out_f32 else torch.bfloat16,
                           device=q.device)
     paged_decode_attention(q, pool, block_table, lengths, scale, shape, workspace, out, stream)
+    return out
+
+
+def decode_step(q, k_new, v_new, pool: Pool, block_table, lengths, scale: float, max_len: int,
+                partition_tokens: int = 0, out_f32: bool = False, workspace=None, out=None, stream=None,
+                engine: int = ENGINE_AUTO):
+    """paged_decode_step with freshly allocated workspace and output (if not given): append the
+    step's new rows k_new, v_new ([B, N, HK, D] bf16) at the slots their positions take in the
+    block table, then attend.  Returns out [B, HQ, N, D]."""
+    import torch
+    B, HQ, N, D = q.shape
+    shape = make_shape(pool, B, HQ, N, block_table.shape[1], max_len, partition_tokens, out_f32, engine)
+    if workspace is None:
+        workspace = torch.empty(paged_decode_workspace_bytes(pool, shape), dtype=torch.uint8,
+                                device=q.device)
+    if out is None:
+        out = torch.empty((B, HQ, N, D), dtype=torch.float32 if out_f32 else torch.bfloat16,
+                          device=q.device)
+    paged_decode_step(q, k_new, v_new, pool, block_table, lengths, scale, shape, workspace, out, stream)
     return out
 
 

@@ -324,9 +324,9 @@ struct Plan {
   bool mfma;
 };
 
-hipError_t launch_plan_partial(const Plan& P, const kvq_pool* pool, int B, hipStream_t st) {
+hipError_t launch_plan_partial(const Plan& P, const kvq_pool* pool, int B, hipStream_t st, bool q_ready = false) {
   if (P.mfma) return kvq::launch_partial_mfma(P.a, pool->desc.head_dim, st);
-  return kvq::launch_partial(P.a, pool->desc.bits, pool->desc.head_dim, P.qvw, B, st);
+  return kvq::launch_partial(P.a, pool->desc.bits, pool->desc.head_dim, P.qvw, B, q_ready, st);
 }
 
 int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, const int32_t* lengths, float scale,
@@ -418,6 +418,58 @@ int paged_decode_attention(const uint16_t* q, const kvq_pool* pool, const int32_
   e = kvq::launch_merge(P.m, shape->batch, st);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return KVQ_OK;
+}
+
+namespace {
+
+int step_partial(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, kvq_pool* pool,
+                 const int32_t* block_table, const int32_t* lengths, float scale, const kvq_decode_shape* shape,
+                 void* workspace, size_t workspace_bytes, void* out, bool need_out, void* stream, Plan* Pout) {
+  Plan& P = *Pout;
+  if (int r = plan(q, pool, block_table, lengths, scale, shape, workspace, workspace_bytes, out, true, need_out, &P))
+    return r;
+  if (!k_new || !v_new) return fail(KVQ_ERR_INVALID, "k_new and v_new must be device pointers");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(KVQ_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
+  const kvq_pool_desc& d = pool->desc;
+  kvq::AppendArgs ap{};
+  ap.k = k_new; ap.v = v_new; ap.slots = nullptr;
+  ap.table = block_table; ap.lengths = lengths;
+  ap.N = shape->q_rows; ap.max_blocks = shape->max_blocks_per_seq; ap.len_cap = P.a.len_cap;
+  ap.k_plane = pool->planes[KVQ_PLANE_K]; ap.v_plane = pool->planes[KVQ_PLANE_V];
+  ap.k_scale = pool->planes[KVQ_PLANE_K_SCALE]; ap.k_bias = pool->planes[KVQ_PLANE_K_BIAS];
+  ap.v_scale = pool->planes[KVQ_PLANE_V_SCALE]; ap.v_bias = pool->planes[KVQ_PLANE_V_BIAS];
+  ap.T = shape->batch * shape->q_rows; ap.HK = d.num_kv_heads; ap.D = d.head_dim; ap.BS = d.block_size;
+  ap.num_slots = (int64_t)d.num_blocks * d.block_size;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = kvq::launch_step_prep(ap, P.a, d.bits, d.head_dim, P.qvw, !P.mfma, shape->batch, st);
+  if (e != hipSuccess) return hip_fail(e, "step launch");
+  e = launch_plan_partial(P, pool, shape->batch, st, true);
+  if (e != hipSuccess) return hip_fail(e, "partial launch");
+  return KVQ_OK;
+}
+
+}  // namespace
+
+int paged_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, kvq_pool* pool,
+                      const int32_t* block_table, const int32_t* lengths, float scale,
+                      const kvq_decode_shape* shape, void* workspace, size_t workspace_bytes, void* out,
+                      void* stream) {
+  Plan P;
+  if (int r = step_partial(q, k_new, v_new, pool, block_table, lengths, scale, shape, workspace, workspace_bytes,
+                           out, true, stream, &P))
+    return r;
+  hipError_t e = kvq::launch_merge(P.m, shape->batch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return KVQ_OK;
+}
+
+int paged_decode_step_partial(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, kvq_pool* pool,
+                              const int32_t* block_table, const int32_t* lengths, float scale,
+                              const kvq_decode_shape* shape, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  Plan P;
+  return step_partial(q, k_new, v_new, pool, block_table, lengths, scale, shape, workspace, workspace_bytes,
+                      nullptr, false, stream, &P);
 }
 
 int kv_gather_debug(const kvq_pool* pool, const int32_t* block_table, const int32_t* lengths, int32_t batch,

@@ -9,7 +9,10 @@ namespace kvq {
 struct AppendArgs {
   const uint16_t* k;      // [T, HK, D] bf16
   const uint16_t* v;
-  const int64_t* slots;   // [T]
+  const int64_t* slots;   // [T]; NULL: a decode step's new rows, slots from the block table
+  const int32_t* table;   // decode step: [B, max_blocks] block table
+  const int32_t* lengths; // decode step: [B], counting the N new rows
+  int32_t N, max_blocks, len_cap;   // decode step: rows per sequence (token = b * N + i), ...
   void* k_plane;          // codes (uint32) or bf16 values
   void* v_plane;
   void* k_scale;          // bf16 planes (affine only)
@@ -72,8 +75,13 @@ hipError_t launch_append(const AppendArgs& a, int bits, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 
 // qvw: query vectors per workgroup (REP * N split into qgroups groups of qvw)
-hipError_t launch_partial(const PartialArgs& a, int bits, int D, int qvw, int B, hipStream_t stream);
+// q_ready: the vector engine's q copy is already in the workspace (decode step)
+hipError_t launch_partial(const PartialArgs& a, int bits, int D, int qvw, int B, bool q_ready, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t stream);
+// decode step: the new rows' append (slots from the block table) and, for the vector engine, the
+// q copy, in one launch
+hipError_t launch_step_prep(const AppendArgs& ap, const PartialArgs& a, int bits, int D, int qvw, bool vector_q,
+                            int B, hipStream_t stream);
 bool partial_supported(int bits, int D, int qvw);
 // most query vectors one wave of the vector engine carries: 8, or 4 where a V lane owns 16 head
 // dims (2-bit pages; bf16 and 8-bit pages at head dim 256)

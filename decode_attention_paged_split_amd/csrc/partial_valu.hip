@@ -48,6 +48,7 @@
 //    end.  Each wave writes one partial per unit of its range, at slot (unit + r) * 8 + wave
 //    (distinct for every (unit, range, wave) because ranges are contiguous and ordered), so
 //    partials stay few whatever the length mix.
+#include "append_rows.hpp"
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -563,15 +564,15 @@ __device__ __forceinline__ int clamp_len(const PartialArgs& a, int b) {
 
 // ------------------------------------------------------------------- q in the codes' pair order
 
-// One workgroup per unit.  For every (scale group g, vector j) a block of q_block_words words:
-// the 32 q pairs of the group's 64 dims in the order the K phase meets the codes, then (affine
-// pages) the f32 sum of q over those 64 dims, the bias term's factor.
+// One workgroup (256 threads) per unit.  For every (scale group g, vector j) a block of
+// q_block_words words: the 32 q pairs of the group's 64 dims in the order the K phase meets the
+// codes, then (affine pages) the f32 sum of q over those 64 dims, the bias term's factor (one
+// wave per block, lane d adds dim d).
 template <int BITS, int D, int QVW>
-__global__ void __launch_bounds__(256) qprep_kernel(PartialArgs a) {
+__device__ __forceinline__ void prep_q(const PartialArgs& a, int64_t u) {
   constexpr int G = D / 64;
   constexpr bool AFF = BITS != 16;
   constexpr int QBS = q_block_words(AFF);
-  const int64_t u = blockIdx.x;
   const int qg = (int)(u % a.qgroups);
   const int hk = (int)((u / a.qgroups) % a.HK);
   const int b = (int)(u / ((int64_t)a.qgroups * a.HK));
@@ -590,13 +591,28 @@ __global__ void __launch_bounds__(256) qprep_kernel(PartialArgs a) {
     out[blk * QBS + p] = (uint32_t)q[lo] | ((uint32_t)q[hi] << 16);
   }
   if constexpr (AFF) {
-    for (int blk = threadIdx.x; blk < G * QVW; blk += blockDim.x) {
+    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+    for (int blk = threadIdx.x >> 6; blk < G * QVW; blk += nw) {
       const int g = blk / QVW, j = blk - g * QVW;
-      const uint16_t* q = qrow(j) + g * 64;
-      float s = 0.0f;
-      for (int d = 0; d < 64; ++d) s += bf16_to_f32(q[d]);
-      out[blk * QBS + 32] = __float_as_uint(s);
+      const float s = block_reduce<OpAdd, 1, 64>(bf16_to_f32(qrow(j)[g * 64 + lane]));
+      if (lane == 0) out[blk * QBS + 32] = __float_as_uint(s);
     }
+  }
+}
+
+template <int BITS, int D, int QVW>
+__global__ void __launch_bounds__(256) qprep_kernel(PartialArgs a) {
+  prep_q<BITS, D, QVW>(a, blockIdx.x);
+}
+
+// Decode step, first launch: blocks [0, na) append the step's new rows (slots from the block
+// table), blocks [na, na + units) prepare q for the vector engine.
+template <int BITS, int D, int QVW, bool VQ>
+__global__ void __launch_bounds__(256) step_prep_kernel(AppendArgs ap, PartialArgs a, int na) {
+  if ((int)blockIdx.x < na) {
+    append_rows<BITS>(ap, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+  } else if constexpr (VQ) {
+    prep_q<BITS, D, QVW>(a, (int64_t)blockIdx.x - na);
   }
 }
 
@@ -784,9 +800,9 @@ partial_stream_kernel(PartialArgs a) {
 // ------------------------------------------------------------------- launch
 
 template <int BITS, int D, int QVW>
-static hipError_t launch_valu(const PartialArgs& a, int B, hipStream_t s) {
+static hipError_t launch_valu(const PartialArgs& a, int B, bool q_ready, hipStream_t s) {
   const unsigned units = (unsigned)((int64_t)B * a.HK * a.qgroups);
-  hipLaunchKernelGGL((qprep_kernel<BITS, D, QVW>), dim3(units), dim3(256), 0, s, a);
+  if (!q_ready) hipLaunchKernelGGL((qprep_kernel<BITS, D, QVW>), dim3(units), dim3(256), 0, s, a);
   if (a.part_tokens > 0) {
     dim3 grid((unsigned)a.num_parts, (unsigned)(a.HK * a.qgroups), (unsigned)B);
     hipLaunchKernelGGL((partial_part_kernel<BITS, D, QVW>), grid, dim3(PV_WAVES * 64), 0, s, a);
@@ -798,24 +814,73 @@ static hipError_t launch_valu(const PartialArgs& a, int B, hipStream_t s) {
 }
 
 template <int BITS, int D>
-static hipError_t launch_valu_d(const PartialArgs& a, int qvw, int B, hipStream_t s) {
+static hipError_t launch_valu_d(const PartialArgs& a, int qvw, int B, bool q_ready, hipStream_t s) {
   switch (qvw) {
-    case 1: return launch_valu<BITS, D, 1>(a, B, s);
-    case 2: return launch_valu<BITS, D, 2>(a, B, s);
-    case 4: return launch_valu<BITS, D, 4>(a, B, s);
+    case 1: return launch_valu<BITS, D, 1>(a, B, q_ready, s);
+    case 2: return launch_valu<BITS, D, 2>(a, B, q_ready, s);
+    case 4: return launch_valu<BITS, D, 4>(a, B, q_ready, s);
     case 8:
-      if constexpr (valu_max_qvw(BITS, D) >= 8) return launch_valu<BITS, D, 8>(a, B, s);
+      if constexpr (valu_max_qvw(BITS, D) >= 8) return launch_valu<BITS, D, 8>(a, B, q_ready, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int BITS>
-static hipError_t launch_valu_b(const PartialArgs& a, int D, int qvw, int B, hipStream_t s) {
+static hipError_t launch_valu_b(const PartialArgs& a, int D, int qvw, int B, bool q_ready, hipStream_t s) {
   switch (D) {
-    case 64: return launch_valu_d<BITS, 64>(a, qvw, B, s);
-    case 128: return launch_valu_d<BITS, 128>(a, qvw, B, s);
-    case 256: return launch_valu_d<BITS, 256>(a, qvw, B, s);
+    case 64: return launch_valu_d<BITS, 64>(a, qvw, B, q_ready, s);
+    case 128: return launch_valu_d<BITS, 128>(a, qvw, B, q_ready, s);
+    case 256: return launch_valu_d<BITS, 256>(a, qvw, B, q_ready, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int BITS, int D, int QVW>
+static hipError_t launch_step_t(const AppendArgs& ap, const PartialArgs& a, bool vq, int B, hipStream_t s) {
+  const int64_t total = (int64_t)ap.T * ap.HK * (ap.D / append_ept(BITS));
+  const int na = (int)((total + 255) / 256);
+  const int nq = vq ? (int)((int64_t)B * a.HK * a.qgroups) : 0;
+  if (na + nq == 0) return hipSuccess;
+  if (vq)
+    hipLaunchKernelGGL((step_prep_kernel<BITS, D, QVW, true>), dim3((unsigned)(na + nq)), dim3(256), 0, s, ap, a, na);
+  else
+    hipLaunchKernelGGL((step_prep_kernel<BITS, D, QVW, false>), dim3((unsigned)na), dim3(256), 0, s, ap, a, na);
+  return hipGetLastError();
+}
+
+template <int BITS, int D>
+static hipError_t launch_step_d(const AppendArgs& ap, const PartialArgs& a, int qvw, bool vq, int B, hipStream_t s) {
+  if (!vq) return launch_step_t<BITS, D, 1>(ap, a, false, B, s);
+  switch (qvw) {
+    case 1: return launch_step_t<BITS, D, 1>(ap, a, true, B, s);
+    case 2: return launch_step_t<BITS, D, 2>(ap, a, true, B, s);
+    case 4: return launch_step_t<BITS, D, 4>(ap, a, true, B, s);
+    case 8:
+      if constexpr (valu_max_qvw(BITS, D) >= 8) return launch_step_t<BITS, D, 8>(ap, a, true, B, s);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int BITS>
+static hipError_t launch_step_b(const AppendArgs& ap, const PartialArgs& a, int D, int qvw, bool vq, int B,
+                                hipStream_t s) {
+  switch (D) {
+    case 64: return launch_step_d<BITS, 64>(ap, a, qvw, vq, B, s);
+    case 128: return launch_step_d<BITS, 128>(ap, a, qvw, vq, B, s);
+    case 256: return launch_step_d<BITS, 256>(ap, a, qvw, vq, B, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_step_prep(const AppendArgs& ap, const PartialArgs& a, int bits, int D, int qvw, bool vector_q,
+                            int B, hipStream_t s) {
+  switch (bits) {
+    case 16: return launch_step_b<16>(ap, a, D, qvw, vector_q, B, s);
+    case 8: return launch_step_b<8>(ap, a, D, qvw, vector_q, B, s);
+    case 4: return launch_step_b<4>(ap, a, D, qvw, vector_q, B, s);
+    case 2: return launch_step_b<2>(ap, a, D, qvw, vector_q, B, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -827,12 +892,12 @@ bool partial_supported(int bits, int D, int qvw) {
   return b && d && q;
 }
 
-hipError_t launch_partial(const PartialArgs& a, int bits, int D, int qvw, int B, hipStream_t s) {
+hipError_t launch_partial(const PartialArgs& a, int bits, int D, int qvw, int B, bool q_ready, hipStream_t s) {
   switch (bits) {
-    case 16: return launch_valu_b<16>(a, D, qvw, B, s);
-    case 8: return launch_valu_b<8>(a, D, qvw, B, s);
-    case 4: return launch_valu_b<4>(a, D, qvw, B, s);
-    case 2: return launch_valu_b<2>(a, D, qvw, B, s);
+    case 16: return launch_valu_b<16>(a, D, qvw, B, q_ready, s);
+    case 8: return launch_valu_b<8>(a, D, qvw, B, q_ready, s);
+    case 4: return launch_valu_b<4>(a, D, qvw, B, q_ready, s);
+    case 2: return launch_valu_b<2>(a, D, qvw, B, q_ready, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -169,6 +169,32 @@ int paged_decode_partial(const uint16_t* q, const kvq_pool* pool, const int32_t*
 int paged_decode_merge(const kvq_pool* pool, const int32_t* lengths, const kvq_decode_shape* shape,
                        const void* workspace, size_t workspace_bytes, void* out, void* stream);
 
+/* One decode step on the device ([P134] cache.ts PagedKVCache.appendDecode: append the step's
+ * rows, then attend over the view that includes them; [P50] paged.ts direct route): the N new
+ * K/V rows of every sequence are quantized on append (same quantizer as kv_append_quantize) into
+ * the slots their positions take in the block table -- row i of sequence b at position
+ * lengths[b] - N + i, block block_table[b, pos / BS], row pos % BS -- and then
+ * paged_decode_attention runs over the updated pool, all on the given stream with no host-side
+ * slot mapping.
+ *   k_new, v_new  device bf16 [B, N, num_kv_heads, head_dim], 16-byte aligned
+ *   other arguments as paged_decode_attention; lengths count the new rows, and the blocks of
+ *   the new positions must already be in the table (allocation is the caller's).
+ * A new row whose position is outside [0, min(max_len, max_blocks_per_seq * BS)) or whose
+ * table entry is outside [0, num_blocks) is not written.
+ * Errors: as paged_decode_attention, and KVQ_ERR_INVALID for NULL or misaligned k_new/v_new. */
+int paged_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, kvq_pool* pool,
+                      const int32_t* block_table, const int32_t* lengths, float scale,
+                      const kvq_decode_shape* shape, void* workspace, size_t workspace_bytes, void* out,
+                      void* stream);
+
+/* The first half of paged_decode_step (append of the new rows and the partial pass, partials
+ * left in the workspace); paged_decode_merge with the same shape completes it.  Same arguments
+ * and errors as paged_decode_step without out. */
+int paged_decode_step_partial(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, kvq_pool* pool,
+                              const int32_t* block_table, const int32_t* lengths, float scale,
+                              const kvq_decode_shape* shape, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* The fetch copy, for indexing tests ([P134] cache.ts pickBlocks / BlockPool.gather):
  * every plane's rows of each sequence in token order.  out_planes[p] (device) receives
  * plane p as [B, num_kv_heads, max_len, width_p] in the plane's element type; rows at

@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for must in ["kv_pool_create", "kv_pool_destroy", "kv_append_quantize", "paged_decode_attention",
-                 "paged_decode_workspace_bytes", "kv_gather_debug", "kvq_last_error"]:
+                 "paged_decode_step", "paged_decode_workspace_bytes", "kv_gather_debug", "kvq_last_error"]:
         assert must in names
 
 
@@ -115,6 +115,19 @@ def _ws_bytes(rows, D, qvecs=0, affine=True):
     if qvecs:
         total = _up(total) + qvecs * (D // 64) * (36 if affine else 32) * 4
     return total
+
+
+def test_decode_step_rejects_missing_rows(lib):
+    p = _FakePool()
+    s = kvq.DecodeShape(2, 16, 1, 40, 1000, 0, 0, 0)
+    need = lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s))
+    P = ctypes.c_void_p(256)
+    assert lib.paged_decode_step(P, None, P, p.handle, P, P, 1.0, ctypes.byref(s), P, need, P, None) == -1
+    assert lib.paged_decode_step(P, ctypes.c_void_p(258), P, p.handle, P, P, 1.0, ctypes.byref(s), P, need, P,
+                                 None) == -1           # misaligned
+    s.q_rows = 9
+    assert lib.paged_decode_step(P, P, P, p.handle, P, P, 1.0, ctypes.byref(s), P, need, P, None) == -2
+    p.close()
 
 
 def test_workspace_too_small_and_null_pointers(lib):
