@@ -106,15 +106,22 @@ int choose_partition(const kvq_pool* pool, const kvq_decode_shape* s) {
 bool use_mfma(const kvq_decode_shape* s) { return s->engine == KVQ_ENGINE_MATRIX; }
 
 // Stream schedule: the most ranges the stream is cut into and the partial slots per (unit, range).
-// Both engines launch 8 waves per compute unit (two per SIMD), all resident at once: the matrix
-// engine gives each wave a range of its own, the vector engine one range per workgroup of 8
-// waves that share its tiles.
+// Every range's waves are resident at once.  The vector engine launches one workgroup of 8 waves
+// (two per SIMD) per compute unit, whose waves share its range's tiles; the matrix engine fits one
+// wave per SIMD (its registers) and gives each of the 4 waves per compute unit a range of its own
+// (a sweep on the c3 / c5 workloads: 8 waves per CU 161 / 1,075 us, 4 waves 151 / 1,064 us,
+// 2 waves 239 / 1,868 us).  KVQ_MFMA_WAVES_PER_CU overrides the 4, for sweeps.
 struct StreamGeom {
   int ranges, sub, min_tokens;
 };
 
 StreamGeom stream_geom(const kvq_decode_shape* s) {
-  if (use_mfma(s)) return {8 * device_cus(), 1, kvq::MFMA_TILE};
+  if (use_mfma(s)) {
+    int per_cu = 4;
+    if (const char* e = std::getenv("KVQ_MFMA_WAVES_PER_CU")) per_cu = std::max(2, std::min(16, std::atoi(e)));
+    per_cu &= ~1;                                 // whole workgroups of two waves
+    return {per_cu * device_cus(), 1, kvq::MFMA_TILE};
+  }
   return {device_cus(), kvq::VALU_STREAM_WAVES, kvq::VALU_STREAM_WAVES * kvq::VALU_TILE};
 }
 

@@ -175,7 +175,7 @@ def test_matrix_engine_limits(lib):
         p = _FakePool(bits=bits, D=D)
         need = lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s))
         if ok:
-            slots = (8 * 256 + 32 * 2) * 16
+            slots = (4 * 256 + 32 * 2) * 16
             assert need == _ws_bytes(slots, D)
         else:
             assert need == 0
