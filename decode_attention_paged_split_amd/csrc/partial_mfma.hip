@@ -19,7 +19,8 @@
 //    the word each lane's k-slot needs.
 //  * softmax: the MFMA result gives every lane one query vector (lane % 16) and four tokens, so
 //    the running max, normaliser and per-group sums are per-lane scalars; the tile max needs two
-//    lane swaps.
+//    lane swaps.  The running max moves only when a score exceeds it by more than 2^8, so the
+//    accumulators are rescaled only then.
 //  * P.V: v_mfma_f32_16x16x32_f16 with A = V^T and B = (p * scale)^T.  V^T comes straight from
 //    the raw 4-bit tile in LDS through ds_read_b64_tr_b4 (a 16 x 16 nibble transpose per 16
 //    lanes); codes become exact f16 (1024 + c, then - 1024 with one packed add).  The weight
@@ -329,10 +330,20 @@ partial_mfma_kernel(PartialArgs a) {
           mt_ = fmaxf(mt_, zz);
         }
       mt_ = qv_max(mt_);
-      const float mnew = fmaxf(m, mt_);
-      const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
-      const float alpha = fast_exp2(m - muse);
-      m = mnew;
+      // the running max moves only when a score exceeds it by more than 2^8 (p <= 256), so the
+      // rescale of the accumulators runs only then (wave-uniform branch)
+      if (__ballot(mt_ > m + 8.0f)) {
+        asm volatile("; running max moves");                      // keeps this a real branch
+        const float mnew = (mt_ > m + 8.0f) ? mt_ : m;
+        const float alpha = (mnew == -INFINITY) ? 1.0f : fast_exp2(m - mnew);
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+#pragma unroll
+        for (int g = 0; g < G; ++g) pbias[g] *= alpha;
+      }
+      const float muse = (m == -INFINITY) ? 0.0f : m;
       float ls = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -342,11 +353,7 @@ partial_mfma_kernel(PartialArgs a) {
         ls += (pv.x + pv.y) + (pv.z + pv.w);
         *reinterpret_cast<float4*>(&S.pt[qv][16 * mt + 4 * ks]) = pv;
       }
-      l = fmaf(l, alpha, ls);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-#pragma unroll
-      for (int g = 0; g < G; ++g) pbias[g] *= alpha;
+      l += ls;
       mf_lds_sync();
       __builtin_amdgcn_sched_barrier(0);
 
