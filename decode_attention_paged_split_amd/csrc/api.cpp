@@ -142,8 +142,8 @@ int validate_shape(const kvq_pool* pool, const kvq_decode_shape* s) {
   if (!s) return fail(KVQ_ERR_INVALID, "decode shape is NULL");
   if (s->batch < 1 || s->num_q_heads < 1 || s->max_blocks_per_seq < 1 || s->max_len < 1)
     return fail(KVQ_ERR_INVALID, "batch, num_q_heads, max_blocks_per_seq and max_len must be positive");
-  if (s->q_rows < 1 || s->q_rows > 8)
-    return fail(KVQ_ERR_UNSUPPORTED, "q_rows must be 1..8 for the direct paged read, got %d", s->q_rows);
+  if (s->q_rows < 1 || s->q_rows > KVQ_MAX_Q_ROWS)
+    return fail(KVQ_ERR_UNSUPPORTED, "q_rows must be 1..%d, got %d", KVQ_MAX_Q_ROWS, s->q_rows);
   if (s->num_q_heads % pool->desc.num_kv_heads != 0)
     return fail(KVQ_ERR_UNSUPPORTED, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
                 s->num_q_heads, pool->desc.num_kv_heads);

@@ -108,10 +108,19 @@ int kv_pool_describe(const kvq_pool* pool, kvq_pool_desc* out);
 int kv_append_quantize(kvq_pool* pool, const uint16_t* k, const uint16_t* v,
                        const int64_t* slots, int32_t num_tokens, void* stream);
 
+/* Most query rows per sequence one call reads straight from the pages.  N <= 8 is the decode
+ * case ([P50] kvq4-decode.ts reads up to 8 rows per sequence directly); larger N is a window of
+ * new rows -- a prefill chunk or a speculative-verify window -- that the pages send through
+ * gather + SDPA ([P50] paged.ts, the gathered route) and this library reads from the pages with the
+ * same kernels: every block of query vectors of a KV head is one more unit of the partial pass,
+ * row i seeing t < lengths[b] - N + i + 1.  The matrix engine suits such windows: its 16-vector
+ * groups put all of a KV head's rows on the matrix cores. */
+#define KVQ_MAX_Q_ROWS 128
+
 typedef struct kvq_decode_shape {
   int32_t batch;               /* B sequences */
   int32_t num_q_heads;         /* HQ, a multiple of the pool's HK */
-  int32_t q_rows;              /* N query rows per sequence, 1..8 */
+  int32_t q_rows;              /* N query rows per sequence, 1..KVQ_MAX_Q_ROWS */
   int32_t max_blocks_per_seq;  /* columns of block_table */
   int32_t max_len;             /* host upper bound on every lengths[b] (sizes the grid) */
   int32_t partition_tokens;    /* tokens per split-K partition; 0 = automatic */
@@ -137,7 +146,7 @@ size_t paged_decode_workspace_bytes(const kvq_pool* pool, const kvq_decode_shape
 /* Partition size the library picks for partition_tokens == 0 (for reporting). */
 int32_t paged_decode_partition_tokens(const kvq_pool* pool, const kvq_decode_shape* shape);
 
-/* Decode attention for N <= 8 query rows per sequence read straight from the pages
+/* Decode attention for N <= KVQ_MAX_Q_ROWS query rows per sequence read straight from the pages
  * ([P50] paged.ts pagedAttentionView.attend, direct route; kvq4-decode.ts):
  *   out[b, h, i, :] = sum_t softmax_t(scale * q[b,h,i,:] . K[b,t,g,:]) V[b,t,g,:]
  * over t < lengths[b] - N + i + 1, with g = h / (HQ / HK) (GQA), K and V the dequantized
@@ -151,7 +160,7 @@ int32_t paged_decode_partition_tokens(const kvq_pool* pool, const kvq_decode_sha
  *                new rows); not checked on the device
  *   workspace    device, >= paged_decode_workspace_bytes(pool, shape) bytes
  *   out          device [B, HQ, N, head_dim], bf16 (round to nearest even) or f32
- * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED (N > 8, HQ % HK != 0),
+ * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED (N > KVQ_MAX_Q_ROWS, HQ % HK != 0),
  * KVQ_ERR_WORKSPACE. */
 int paged_decode_attention(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table,
                            const int32_t* lengths, float scale, const kvq_decode_shape* shape,

@@ -86,7 +86,7 @@ class _FakePool:
         kvq.kv_pool_destroy(self.handle)
 
 
-@pytest.mark.parametrize("mut,code", [(dict(q_rows=9), -2), (dict(q_rows=0), -2), (dict(num_q_heads=5), -2),
+@pytest.mark.parametrize("mut,code", [(dict(q_rows=129), -2), (dict(q_rows=0), -2), (dict(num_q_heads=5), -2),
                                       (dict(batch=0), -1), (dict(max_len=0), -1),
                                       (dict(max_blocks_per_seq=1, max_len=1000), -6),
                                       (dict(partition_tokens=-1), -1), (dict(engine=3), -1),
@@ -125,7 +125,7 @@ def test_decode_step_rejects_missing_rows(lib):
     assert lib.paged_decode_step(P, None, P, p.handle, P, P, 1.0, ctypes.byref(s), P, need, P, None) == -1
     assert lib.paged_decode_step(P, ctypes.c_void_p(258), P, p.handle, P, P, 1.0, ctypes.byref(s), P, need, P,
                                  None) == -1           # misaligned
-    s.q_rows = 9
+    s.q_rows = 129
     assert lib.paged_decode_step(P, P, P, p.handle, P, P, 1.0, ctypes.byref(s), P, need, P, None) == -2
     p.close()
 
