@@ -50,10 +50,10 @@ int validate_desc(const kvq_pool_desc* d) {
                 d->num_blocks, d->num_kv_heads, d->block_size, d->head_dim);
   if (!(d->bits == 16 || d->bits == 8 || d->bits == 4 || d->bits == 2))
     return fail(KVQ_ERR_UNSUPPORTED, "bits must be 16 (bf16 pages) or 8, 4, 2 (affine), got %d", d->bits);
-  if (d->group_size != 64)
-    return fail(KVQ_ERR_UNSUPPORTED, "group_size must be 64, got %d", d->group_size);
   if (d->head_dim % 64 != 0 || d->head_dim > 256)
     return fail(KVQ_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256, got %d", d->head_dim);
+  if (!(d->group_size == 32 || d->group_size == 64 || d->group_size == 128) || d->head_dim % d->group_size != 0)
+    return fail(KVQ_ERR_UNSUPPORTED, "group_size must be 32, 64 or 128 and divide head_dim, got %d", d->group_size);
   const size_t rows = (size_t)d->num_blocks * d->num_kv_heads * d->block_size;
   if (rows >= (size_t)1 << 31)
     return fail(KVQ_ERR_UNSUPPORTED, "num_blocks * num_kv_heads * block_size must stay below 2^31 rows");
@@ -84,8 +84,8 @@ int device_cus() {
 constexpr int MAX_PARTS = 8192;
 
 // query vectors per workgroup: the largest power of two <= kvq::valu_max_qvw dividing REP * N
-int qvw_for(int qv, int bits, int D) {
-  for (int w = kvq::valu_max_qvw(bits, D); w >= 1; w /= 2)
+int qvw_for(int qv, int bits, int D, int gs) {
+  for (int w = kvq::valu_max_qvw(bits, D, gs); w >= 1; w /= 2)
     if (qv % w == 0) return w;
   return 1;
 }
@@ -128,7 +128,7 @@ StreamGeom stream_geom(const kvq_decode_shape* s) {
 // query vectors per workgroup (vector ALU) or per wave (matrix cores, padded to 16)
 int qvw_of(const kvq_pool* pool, const kvq_decode_shape* s) {
   const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
-  return use_mfma(s) ? kvq::MFMA_QVW : qvw_for(qv, pool->desc.bits, pool->desc.head_dim);
+  return use_mfma(s) ? kvq::MFMA_QVW : qvw_for(qv, pool->desc.bits, pool->desc.head_dim, pool->desc.group_size);
 }
 
 int qgroups_of(const kvq_pool* pool, const kvq_decode_shape* s) {
@@ -164,12 +164,14 @@ int validate_shape(const kvq_pool* pool, const kvq_decode_shape* s) {
   if (s->engine < KVQ_ENGINE_AUTO || s->engine > KVQ_ENGINE_MATRIX)
     return fail(KVQ_ERR_INVALID, "engine must be 0 (automatic), 1 (vector ALU) or 2 (matrix cores)");
   if (use_mfma(s)) {
-    if (!kvq::mfma_supported(pool->desc.bits, pool->desc.head_dim))
-      return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core engine reads 4-bit pages with head_dim 128 or 256");
+    if (!kvq::mfma_supported(pool->desc.bits, pool->desc.head_dim, pool->desc.group_size))
+      return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core engine reads 4-bit pages with head_dim 128 or 256 and "
+                                       "group_size 64");
     if (pt > 0)
       return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core engine runs the balanced stream schedule only "
                                        "(partition_tokens = 0)");
-  } else if (!kvq::partial_supported(pool->desc.bits, pool->desc.head_dim, qvw_for(qv, pool->desc.bits, pool->desc.head_dim))) {
+  } else if (!kvq::partial_supported(pool->desc.bits, pool->desc.head_dim, pool->desc.group_size,
+                                     qvw_for(qv, pool->desc.bits, pool->desc.head_dim, pool->desc.group_size))) {
     return fail(KVQ_ERR_UNSUPPORTED, "no kernel for bits=%d D=%d", pool->desc.bits, pool->desc.head_dim);
   }
   return KVQ_OK;
@@ -178,7 +180,7 @@ int validate_shape(const kvq_pool* pool, const kvq_decode_shape* s) {
 // Partials: fixed partitions hold [B, HQ, N, parts] rows; the stream schedule holds
 // (ranges + units) * sub slots of QVW vectors (slot = (unit + range) * sub + wave in range).  Each partial row is D floats of
 // unnormalised output plus (max, normaliser).  The vector engine adds its copy of q in the
-// codes' pair order, [units, D/64, QVW] blocks of q_block_words words.
+// codes' pair order, D/32 blocks of Q_BLOCK_WORDS words per query vector.
 struct WsLayout {
   size_t ml_off, qp_off, total;
 };
@@ -200,7 +202,7 @@ WsLayout workspace_layout(const kvq_pool* pool, const kvq_decode_shape* s, int p
   if (!use_mfma(s)) {
     const size_t qv = (size_t)s->batch * pool->desc.num_kv_heads * qgroups_of(pool, s) * qvw_of(pool, s);
     L.qp_off = up(L.total);
-    L.total = L.qp_off + qv * (pool->desc.head_dim / 64) * kvq::q_block_words(pool->desc.bits != 16) * 4;
+    L.total = L.qp_off + qv * (pool->desc.head_dim / 32) * kvq::Q_BLOCK_WORDS * 4;
   }
   return L;
 }
@@ -305,7 +307,7 @@ int kv_append_quantize(kvq_pool* pool, const uint16_t* k, const uint16_t* v, con
   a.k_plane = pool->planes[KVQ_PLANE_K]; a.v_plane = pool->planes[KVQ_PLANE_V];
   a.k_scale = pool->planes[KVQ_PLANE_K_SCALE]; a.k_bias = pool->planes[KVQ_PLANE_K_BIAS];
   a.v_scale = pool->planes[KVQ_PLANE_V_SCALE]; a.v_bias = pool->planes[KVQ_PLANE_V_BIAS];
-  a.T = num_tokens; a.HK = d.num_kv_heads; a.D = d.head_dim; a.BS = d.block_size;
+  a.T = num_tokens; a.HK = d.num_kv_heads; a.D = d.head_dim; a.BS = d.block_size; a.group = d.group_size;
   a.num_slots = (int64_t)d.num_blocks * d.block_size;
   hipError_t e = kvq::launch_append(a, d.bits, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");
@@ -333,7 +335,8 @@ struct Plan {
 
 hipError_t launch_plan_partial(const Plan& P, const kvq_pool* pool, int B, hipStream_t st, bool q_ready = false) {
   if (P.mfma) return kvq::launch_partial_mfma(P.a, pool->desc.head_dim, st);
-  return kvq::launch_partial(P.a, pool->desc.bits, pool->desc.head_dim, P.qvw, B, q_ready, st);
+  return kvq::launch_partial(P.a, pool->desc.bits, pool->desc.head_dim, pool->desc.group_size, P.qvw, B, q_ready,
+                             st);
 }
 
 int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, const int32_t* lengths, float scale,
@@ -446,9 +449,10 @@ int step_partial(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new
   ap.k_scale = pool->planes[KVQ_PLANE_K_SCALE]; ap.k_bias = pool->planes[KVQ_PLANE_K_BIAS];
   ap.v_scale = pool->planes[KVQ_PLANE_V_SCALE]; ap.v_bias = pool->planes[KVQ_PLANE_V_BIAS];
   ap.T = shape->batch * shape->q_rows; ap.HK = d.num_kv_heads; ap.D = d.head_dim; ap.BS = d.block_size;
+  ap.group = d.group_size;
   ap.num_slots = (int64_t)d.num_blocks * d.block_size;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = kvq::launch_step_prep(ap, P.a, d.bits, d.head_dim, P.qvw, !P.mfma, shape->batch, st);
+  hipError_t e = kvq::launch_step_prep(ap, P.a, d.bits, d.head_dim, d.group_size, P.qvw, !P.mfma, shape->batch, st);
   if (e != hipSuccess) return hip_fail(e, "step launch");
   e = launch_plan_partial(P, pool, shape->batch, st, true);
   if (e != hipSuccess) return hip_fail(e, "partial launch");

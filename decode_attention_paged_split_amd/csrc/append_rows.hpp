@@ -2,8 +2,8 @@
 // kernel and the decode-step kernel).
 //
 // Follows "@mlx-bun/inference 0.0.0-stage -> 1.0.0", diff page 134 (src/state/paged/
-// cache.ts): BlockPool.writeBlock quantizes each appended row per group of 64 elements
-// along the head dim and slice-updates codes, scales and biases at [block, head, row];
+// cache.ts): BlockPool.writeBlock quantizes each appended row per group of groupSize elements
+// (PagedQuantization; 32, 64 or 128 here) along the head dim and slice-updates codes, scales and biases at [block, head, row];
 // PagedKVCache.append maps each new token to (physical block, row).  The slot of a token is
 // either the caller's (one int64 slot = block * block_size + row per token) or, for a decode
 // step, the one its position takes in the block table: the N new rows of sequence b are
@@ -20,7 +20,7 @@
 // codes match any correctly rounded f32 implementation exactly.
 //
 // Mapping: one thread per EPT consecutive elements of one (token, head) row (EPT = 8,
-// or 16 at 2 bits so that a thread owns whole words); the 64/EPT threads of a group are
+// or 16 at 2 bits so that a thread owns whole words); the GS/EPT threads of a group are
 // adjacent lanes and reduce min/max with DPP.  Loads are 16-byte, coalesced along the row.
 #pragma once
 
@@ -42,11 +42,12 @@ __device__ __forceinline__ int64_t decode_slot(const AppendArgs& a, int64_t tok)
   return (int64_t)phys * a.BS + t % a.BS;
 }
 
-// one thread per EPT elements of one (token, head) row; gid indexes (token, head, chunk)
-template <int BITS>
+// one thread per EPT elements of one (token, head) row; gid indexes (token, head, chunk); GS is
+// the scale-group size (affine pages; bf16 rows ignore it)
+template <int BITS, int GS>
 __device__ __forceinline__ void append_rows(const AppendArgs& a, int64_t gid) {
   constexpr int EPT = append_ept(BITS);         // elements per thread
-  constexpr int TPG = 64 / EPT;                 // threads per group of 64
+  constexpr int TPG = GS / EPT;                 // threads per scale group
   const int chunks = a.D / EPT;
   const int64_t total = (int64_t)a.T * a.HK * chunks;
   const bool live = gid < total;
@@ -122,7 +123,7 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int64_t gid) {
 #pragma unroll
         for (int j = 0; j < NWORDS; ++j) dst[j] = out[j];
         if ((chunk % TPG) == 0) {
-          const int G = a.D / 64;
+          const int G = a.D / GS;
           const int grp = chunk / TPG;
           uint16_t* sp = static_cast<uint16_t*>(kv ? a.v_scale : a.k_scale);
           uint16_t* bp = static_cast<uint16_t*>(kv ? a.v_bias : a.k_bias);

@@ -20,6 +20,7 @@ struct AppendArgs {
   void* v_scale;
   void* v_bias;
   int32_t T, HK, D, BS;
+  int32_t group;          // scale-group size (affine pages)
   int64_t num_slots;      // num_blocks * BS
 };
 
@@ -44,7 +45,7 @@ struct PartialArgs {
   const int32_t* lengths;   // [B]
   float* opart;             // [B, HQ, N, P, D] f32, unnormalised
   float* ml;                // [B, HQ, N, P, 2] f32: running max (log2 units), normaliser
-  uint32_t* qp;             // vector engine: [units, D/64, QVW, q_block_words] q in the codes' order
+  uint32_t* qp;             // vector engine: [units, D/32 blocks x QVW, Q_BLOCK_WORDS] q in the codes' order
   float scale_log2e;        // softmax scale * log2(e)
   int32_t HQ, HK, N, BS, bs_shift, max_blocks, num_blocks, max_len;
   int32_t part_tokens;      // > 0: fixed partitions of this many tokens; 0: balanced stream
@@ -67,29 +68,35 @@ struct MergeArgs {
   int32_t batch, HK, qgroups, qvw, num_ranges, range_sub, min_tokens;   // stream (part_tokens == 0)
 };
 
-// words per (scale group, query vector) block of the vector engine's q copy: 32 bf16 pairs,
-// then (affine pages) the f32 sum of q over the group
-constexpr int q_block_words(bool affine) { return affine ? 36 : 32; }
+// words per block of the vector engine's q copy: 16 bf16 pairs of one query vector, then (last
+// block of a scale group, affine pages) the f32 sum of q over the group, then padding; a query
+// vector takes head_dim / 32 blocks
+constexpr int Q_BLOCK_WORDS = 20;
 
 hipError_t launch_append(const AppendArgs& a, int bits, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 
 // qvw: query vectors per workgroup (REP * N split into qgroups groups of qvw)
-// q_ready: the vector engine's q copy is already in the workspace (decode step)
-hipError_t launch_partial(const PartialArgs& a, int bits, int D, int qvw, int B, bool q_ready, hipStream_t stream);
+// q_ready: the vector engine's q copy is already in the workspace (decode step); gs: the pool's
+// scale-group size (affine pages)
+hipError_t launch_partial(const PartialArgs& a, int bits, int D, int gs, int qvw, int B, bool q_ready,
+                          hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t stream);
 // decode step: the new rows' append (slots from the block table) and, for the vector engine, the
 // q copy, in one launch
-hipError_t launch_step_prep(const AppendArgs& ap, const PartialArgs& a, int bits, int D, int qvw, bool vector_q,
-                            int B, hipStream_t stream);
-bool partial_supported(int bits, int D, int qvw);
+hipError_t launch_step_prep(const AppendArgs& ap, const PartialArgs& a, int bits, int D, int gs, int qvw,
+                            bool vector_q, int B, hipStream_t stream);
+bool partial_supported(int bits, int D, int gs, int qvw);
 // most query vectors one wave of the vector engine carries: 8, or 4 where a V lane owns 16 head
-// dims (2-bit pages; bf16 and 8-bit pages at head dim 256)
-constexpr int valu_max_qvw(int bits, int D) { return (bits == 2 || (D == 256 && bits >= 8)) ? 4 : 8; }
+// dims (2-bit pages; bf16 and 8-bit pages at head dim 256) or a row has 8 scale groups (the
+// per-lane bias sums, vectors x groups, stay within 32 registers)
+constexpr int valu_max_qvw(int bits, int D, int gs) {
+  return (bits == 2 || (D == 256 && bits >= 8) || (bits != 16 && D / gs > 4)) ? 4 : 8;
+}
 
 // matrix-core engine (4-bit pages, head dim 128/256, stream schedule, 16 query vectors per wave,
 // 64-token tiles)
-bool mfma_supported(int bits, int D);
+bool mfma_supported(int bits, int D, int gs);
 hipError_t launch_partial_mfma(const PartialArgs& a, int D, hipStream_t s);
 constexpr int MFMA_QVW = 16;
 constexpr int MFMA_TILE = 64;

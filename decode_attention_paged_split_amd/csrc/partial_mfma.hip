@@ -439,7 +439,7 @@ partial_mfma_kernel(PartialArgs a) {
   }
 }
 
-bool mfma_supported(int bits, int D) { return bits == 4 && (D == 128 || D == 256); }
+bool mfma_supported(int bits, int D, int gs) { return bits == 4 && gs == 64 && (D == 128 || D == 256); }
 
 hipError_t launch_partial_mfma(const PartialArgs& a, int D, hipStream_t s) {
   dim3 grid((unsigned)(a.num_ranges / MF_WAVES));

@@ -65,7 +65,8 @@ def test_pool_bytes_match_the_layout(lib, name, expect):
         assert kvq.kv_pool_plane_bytes(d, 5) == rows * (w.D // 64) * 2
 
 
-@pytest.mark.parametrize("field,value,code", [("bits", 3, -2), ("bits", 32, -2), ("group_size", 32, -2),
+@pytest.mark.parametrize("field,value,code", [("bits", 3, -2), ("bits", 32, -2), ("group_size", 48, -2),
+                                              ("group_size", 256, -2), ("group_size", 16, -2),
                                               ("head_dim", 96, -2), ("head_dim", 512, -2),
                                               ("num_blocks", 0, -1), ("block_size", 0, -1)])
 def test_pool_descriptor_rejected(lib, field, value, code):
@@ -75,6 +76,20 @@ def test_pool_descriptor_rejected(lib, field, value, code):
         kvq.kv_pool_wrap(d, [16] * 6)
     assert e.value.code == code
     assert lib.kvq_last_error().decode()
+
+
+@pytest.mark.parametrize("group,D,ok", [(32, 256, True), (128, 256, True), (128, 128, True), (128, 64, False),
+                                         (32, 64, True)])
+def test_group_sizes(lib, group, D, ok):
+    d = kvq.PoolDesc(4, 2, 16, D, 4, group)
+    if ok:
+        h = kvq.kv_pool_wrap(d, [16] * 6)
+        assert kvq.kv_pool_plane_bytes(d, 3) == 4 * 2 * 16 * (D // group) * 2
+        kvq.kv_pool_destroy(h)
+    else:
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kv_pool_wrap(d, [16] * 6)
+        assert e.value.code == -2
 
 
 class _FakePool:
@@ -110,10 +125,10 @@ def _up(x):
 
 def _ws_bytes(rows, D, qvecs=0, affine=True):
     """partials: rows of D floats (padded to 256 B) + rows of (max, normaliser); then the vector
-    engine's q copy (per query vector and 64-dim group a block of 36 words, 32 on bf16 pages)"""
+    engine's q copy (per query vector D/32 blocks of 20 words)"""
     total = _up(rows * D * 4) + rows * 2 * 4
     if qvecs:
-        total = _up(total) + qvecs * (D // 64) * (36 if affine else 32) * 4
+        total = _up(total) + qvecs * (D // 32) * 20 * 4
     return total
 
 
@@ -180,3 +195,7 @@ def test_matrix_engine_limits(lib):
         else:
             assert need == 0
         p.close()
+    d = kvq.PoolDesc(64, 2, 32, 256, 4, 32)
+    h = kvq.kv_pool_wrap(d, [256] * 6)
+    assert lib.paged_decode_workspace_bytes(h, ctypes.byref(s)) == 0      # matrix engine: group 64 only
+    kvq.kv_pool_destroy(h)

@@ -125,8 +125,8 @@ MUTATIONS = {
 PINS = [
     (TQ.test_packing_worked_words, ()),
     (TQ.test_quantizer_worked_groups, ()),
-    (TQ.test_quantize_error_bound, (8, "c3")),
-    (TQ.test_quantize_error_bound, (4, "c3")),
+    (TQ.test_quantize_error_bound, (8, "c3", 64)),
+    (TQ.test_quantize_error_bound, (4, "c3", 32)),
     (TA.test_matches_torch_sdpa, (4, 64, 3)),
     (TA.test_closed_forms, ()),
     (TA.test_split_merge_equals_two_pass, (64,)),

@@ -168,22 +168,23 @@ def test_quantizer_against_exact_rationals(bits):
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("wl", ["c3", "c5", "c2"])
-def test_quantize_error_bound(bits, wl):
+@pytest.mark.parametrize("group", [64, 32, 128])
+def test_quantize_error_bound(bits, wl, group):
     """|x - dequant(quant(x))| <= scale / 2 for every element; codes within [0, 2^bits - 1];
     the group minimum maps to code 0 and the maximum to the top code (bits <= 4) or within
     2 of it (8 bits, where the rounded-up scale can leave the top code unused)."""
     w = make_workload(wl, B=2, len_lo=300, len_hi=400, D=256, HK=2)
     k, v = w.kv(0)
     for x in (k, v):
-        words, s, bb = quant.quantize(x, bits)
+        words, s, bb = quant.quantize(x, bits, group)
         codes = quant.unpack(words, bits)
         n = (1 << bits) - 1
         assert codes.max() <= n
         xf = bf16.to_f64(x)
-        deq = quant.dequantize(words, s, bb, bits)
-        half = np.repeat(bf16.to_f64(s), 64, axis=-1) / 2
+        deq = quant.dequantize(words, s, bb, bits, group)
+        half = np.repeat(bf16.to_f64(s), group, axis=-1) / 2
         assert np.all(np.abs(xf - deq) <= half)
-        g = xf.reshape(xf.shape[:-1] + (4, 64))
+        g = xf.reshape(xf.shape[:-1] + (256 // group, group))
         cg = codes.reshape(g.shape)
         amin, amax = g.argmin(-1), g.argmax(-1)
         assert np.all(np.take_along_axis(cg, amin[..., None], -1) == 0)
@@ -192,6 +193,23 @@ def test_quantize_error_bound(bits, wl):
             assert np.all(top == n)
         else:
             assert np.all(top >= n - 2)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_group_size_is_a_partition_of_the_row(bits):
+    """Scale groups are independent: quantizing a row with groups of G equals quantizing each
+    G-element slice as a one-group row (checked for G = 32, 64, 128 against G = slice length), and
+    the packed words do not depend on the grouping beyond the codes themselves."""
+    rng = np.random.default_rng(40 + bits)
+    x = bf16.rne(rng.standard_normal((6, 256)).astype(np.float32) * 3)
+    for G in (32, 64, 128):
+        codes, s, b = quant.quantize_codes(x, bits, G)
+        for gi in range(256 // G):
+            c1, s1, b1 = quant.quantize_codes(x[:, gi * G:(gi + 1) * G], bits, G)
+            assert np.array_equal(codes[:, gi * G:(gi + 1) * G], c1)
+            assert np.array_equal(s[:, gi], s1[:, 0]) and np.array_equal(b[:, gi], b1[:, 0])
+        words, _, _ = quant.quantize(x, bits, G)
+        assert np.array_equal(words, quant.pack(codes, bits))
 
 
 def test_effective_bytes_ratio_from_the_page_header():

@@ -161,11 +161,12 @@ def make_workload(name: str, *, B: Optional[int] = None, len_lo: Optional[int] =
                   len_hi: Optional[int] = None, BS: Optional[int] = None, seed: int = 0,
                   bits: Optional[int] = None, N: Optional[int] = None,
                   HQ: Optional[int] = None, HK: Optional[int] = None,
-                  D: Optional[int] = None) -> Workload:
-    """Build a named workload, optionally shrunk (fewer / shorter sequences) for tests."""
+                  D: Optional[int] = None, group: Optional[int] = None) -> Workload:
+    """Build a named workload, optionally shrunk (fewer / shorter sequences) or reshaped for
+    tests (the draws depend only on the seed, the workload's key and the shapes)."""
     s = WORKLOADS[name]
     over = {k: v for k, v in dict(B=B, len_lo=len_lo, len_hi=len_hi, BS=BS, bits=bits, N=N,
-                                   HQ=HQ, HK=HK, D=D).items() if v is not None}
+                                   HQ=HQ, HK=HK, D=D, group=group).items() if v is not None}
     s = dataclasses.replace(s, **over)
     rng = np.random.default_rng(np.random.SeedSequence([seed, s.key]))
     lengths = rng.integers(s.len_lo, s.len_hi + 1, size=s.B).astype(np.int64)
