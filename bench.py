@@ -45,7 +45,8 @@ def kernel_source_hash() -> str:
     """Hash of the sources that decide what the partial kernel reads and writes (its code and the
     host-side launch geometry)."""
     h = hashlib.sha256()
-    for f in ("partial_valu.hip", "device_common.hpp", "kernels.hpp", "api.cpp"):
+    for f in ("partial_valu.hip", "partial_valu_impl.hpp", "partial_valu_b4.hip", "device_common.hpp",
+              "kernels.hpp", "api.cpp"):
         with open(os.path.join(ROOT, "decode_attention_paged_split_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

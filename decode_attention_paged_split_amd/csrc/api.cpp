@@ -107,19 +107,20 @@ bool use_mfma(const kvq_decode_shape* s) { return s->engine == KVQ_ENGINE_MATRIX
 
 // Stream schedule: the most ranges the stream is cut into and the partial slots per (unit, range).
 // Every range's waves are resident at once.  The vector engine launches one workgroup of 8 waves
-// (two per SIMD) per compute unit, whose waves share its range's tiles; the matrix engine fits one
-// wave per SIMD (its registers) and gives each of the 4 waves per compute unit a range of its own
-// (a sweep on the c3 / c5 workloads: 8 waves per CU 161 / 1,075 us, 4 waves 151 / 1,064 us,
-// 2 waves 239 / 1,868 us).  KVQ_MFMA_WAVES_PER_CU overrides the 4, for sweeps.
+// (two per SIMD) per compute unit, whose waves share its range's tiles.  The matrix engine runs two
+// waves per SIMD: at head dim 256 a workgroup of two waves (one per half of the head dim) works one
+// range, 4 workgroups per compute unit; at head dim 128 each of 8 waves per compute unit works a
+// range of its own.  KVQ_MFMA_RANGES_PER_CU overrides the 4 / 8, for sweeps.
 struct StreamGeom {
   int ranges, sub, min_tokens;
 };
 
-StreamGeom stream_geom(const kvq_decode_shape* s) {
+StreamGeom stream_geom(const kvq_pool* pool, const kvq_decode_shape* s) {
   if (use_mfma(s)) {
-    int per_cu = 4;
-    if (const char* e = std::getenv("KVQ_MFMA_WAVES_PER_CU")) per_cu = std::max(2, std::min(16, std::atoi(e)));
-    per_cu &= ~1;                                 // whole workgroups of two waves
+    const bool split = pool->desc.head_dim == 256;
+    int per_cu = split ? 4 : 8;
+    if (const char* e = std::getenv("KVQ_MFMA_RANGES_PER_CU")) per_cu = std::max(2, std::min(16, std::atoi(e)));
+    if (!split) per_cu &= ~1;                     // whole workgroups of two independent waves
     return {per_cu * device_cus(), 1, kvq::MFMA_TILE};
   }
   return {device_cus(), kvq::VALU_STREAM_WAVES, kvq::VALU_STREAM_WAVES * kvq::VALU_TILE};
@@ -192,7 +193,7 @@ WsLayout workspace_layout(const kvq_pool* pool, const kvq_decode_shape* s, int p
     rows = (size_t)s->batch * s->num_q_heads * s->q_rows * parts;
   } else {
     const size_t units = (size_t)s->batch * pool->desc.num_kv_heads * qgroups_of(pool, s);
-    const StreamGeom sg = stream_geom(s);
+    const StreamGeom sg = stream_geom(pool, s);
     rows = ((size_t)sg.ranges + units) * sg.sub * qvw_of(pool, s);
   }
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -378,7 +379,7 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   a.max_blocks = shape->max_blocks_per_seq; a.num_blocks = d.num_blocks; a.max_len = shape->max_len;
   a.part_tokens = pt; a.num_parts = parts; a.qgroups = qgroups_of(pool, shape);
   a.len_cap = (int)std::min<long>(shape->max_len, (long)shape->max_blocks_per_seq * d.block_size);
-  const StreamGeom sg = stream_geom(shape);
+  const StreamGeom sg = stream_geom(pool, shape);
   a.batch = shape->batch; a.num_ranges = sg.ranges; a.range_sub = sg.sub; a.min_tokens = sg.min_tokens;
 
   kvq::MergeArgs& m = P->m;

@@ -183,14 +183,15 @@ def test_automatic_schedule_is_the_balanced_stream(lib, monkeypatch):
 
 
 def test_matrix_engine_limits(lib):
-    """The matrix-core engine reads 4-bit pages at head dim 128/256 on the stream schedule; its
-    workspace holds 16 query vectors per slot."""
+    """The matrix-core engine reads 4-bit pages at head dim 128/256 on the stream schedule (4
+    ranges per compute unit at head dim 256, a two-wave workgroup each; 8 at 128, a wave each);
+    its workspace holds 16 query vectors per slot."""
     s = kvq.DecodeShape(32, 16, 1, 1100, 32197, 0, 0, 2)
     for bits, D, ok in [(4, 256, True), (4, 128, True), (8, 256, False), (16, 128, False), (4, 64, False)]:
         p = _FakePool(bits=bits, D=D)
         need = lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s))
         if ok:
-            slots = (4 * 256 + 32 * 2) * 16
+            slots = ((4 if D == 256 else 8) * 256 + 32 * 2) * 16
             assert need == _ws_bytes(slots, D)
         else:
             assert need == 0
