@@ -34,6 +34,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# MI355X published dense fp32 vector peak (256 CUs x 4 SIMDs x 16 lanes x 2 FMA x 2 flop x 2.4 GHz:
+# packed FP32).  Code here issues no packed FP32, so the vector path's attainable ceiling is half
+# of it for its f32 FMAs (its bf16 dot2 steps still do 2 MACs per lane-op).
+VALU_PEAK_TFLOPS = 157.3
 METRIC = "effective KV GB/s (% of HBM peak) + µs per decode step, 4-bit paged D=256"
 
 
@@ -237,13 +241,24 @@ def main():
     part_s = float(np.mean(par)) * 1e-3
     achieved = eff / part_s / 1e9
     src_hash = kernel_source_hash() if args.engine != "matrix" else None
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+    # binding roof of the partial pass: HBM (effective bytes / 8 TB/s) or the vector ALU
+    # (2 * REP * N * D multiply-adds per cached token and KV head / the fp32 vector peak)
+    flops = w.attention_flops()
+    hbm_floor = eff / (HBM_PEAK_GBS * 1e9)
+    alu_floor = flops / (VALU_PEAK_TFLOPS * 1e12)
+    hbm = {"achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(achieved / HBM_PEAK_GBS, 4), "floor_us": round(hbm_floor * 1e6, 2)}
+    alu = {"achieved": round(flops / part_s / 1e12, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+           "frac": round(flops / part_s / 1e12 / VALU_PEAK_TFLOPS, 4), "floor_us": round(alu_floor * 1e6, 2)}
+    top = alu if (alu_floor > hbm_floor and args.engine != "matrix") else hbm
+    roof = {"bound": "alu" if top is alu else "hbm", "achieved": top["achieved"], "peak": top["peak"],
+            "unit": top["unit"], "frac": top["frac"],
             "traffic": traffic_from_profiles(w.name, src_hash) if src_hash else None,
             "kernel": "partial pass: append of the step's rows + q copy + partial kernel "
                       "(events around paged_decode_step_partial)",
             "kernel_us": round(part_s * 1e6, 2),
-            "algorithmic_bytes_per_launch": eff, "kernel_source_hash": src_hash}
+            "algorithmic_bytes_per_launch": eff, "algorithmic_flops_per_launch": flops,
+            "hbm": hbm, "alu": alu, "kernel_source_hash": src_hash}
 
     variants = {}
     if args.engine == "auto" and w.bits == 4 and w.D in (128, 256) and args.partition_tokens == 0:
@@ -265,7 +280,11 @@ def main():
         par_m = float(np.mean([o.elapsed_time(m) for o, m in zip([e0m] + endm[:-1], midm)]))
         variants["matrix_engine"] = {
             "value": round(eff / (ms_m * 1e-3) / 1e9, 1), "unit": "GB/s", "us_per_step": round(ms_m * 1e3, 2),
-            "partial_us": round(par_m * 1e3, 2), "partial_frac_hbm": round(eff / (par_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "pct_hbm_peak": round(100 * eff / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "partial_us": round(par_m * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(eff / (par_m * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(eff / (par_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "mfma_tflops": round(flops / (par_m * 1e-3) / 1e12, 2)},
             "note": "engine=2: MFMA q.k and P.V, 4-bit pages; not the default path"}
         log(f"[bench] matrix engine: {ms_m * 1e3:.1f} us/step (partial {par_m * 1e3:.1f})")
     rec = {

@@ -148,6 +148,12 @@ class Workload:
         t = np.arange(start, stop, dtype=np.int64)
         return self.table[b, t // self.BS].astype(np.int64) * self.BS + t % self.BS
 
+    def attention_flops(self) -> int:
+        """Multiply-add flops of one decode step's attention: 2 * (q.k + p.v) MACs, i.e.
+        sum(len) * HK * 2 * (2 * REP * N * D) (every cached token meets every query vector of its
+        KV head; causal masking of the last N - 1 tokens is not discounted)."""
+        return int(self.lengths.sum()) * self.HK * 2 * (2 * self.REP * self.N * self.D)
+
     def effective_bytes(self) -> int:
         """K/V bytes one decode step must read: sum(len) * HK * (K + V bytes per token row)."""
         if self.bits == 16:
