@@ -5,9 +5,11 @@
 // (o_p, m_p, l_p) over partitions p, out = sum_p e^(m_p - M) o_p / sum_p e^(m_p - M) l_p with
 // M = max_p m_p; partitions whose max is -inf (no visible token) are skipped.  Maxima are in
 // log2 units here (the partial kernel scales scores by log2(e)), so the weights are exp2.
-// One workgroup per output row: the partition weights are computed once into LDS, then each
-// thread accumulates four head dims over a stride of the partials (several loads in flight per
-// thread) and the strides' sums are added in LDS.  Output is bf16 (round to nearest even) or f32.
+// One workgroup per output row, one pass over the partials: thread (stream s, dim lane dl) owns
+// head dims 4 dl .. 4 dl + 3 and partials s, s + S, ...; it loads each partial's (m, l) and o
+// together and folds them into a running (max, sum of weights, weighted o) (the weights are
+// rescaled when the max moves), and the S streams' states are combined in LDS the same way.
+// Output is bf16 (round to nearest even) or f32.
 // Stream schedule: the stream of T tokens is cut into R = min(num_ranges, ceil(T / min_tokens))
 // ranges; a unit's partials sit in range_sub consecutive slots per range it meets, from slot
 // (unit + first range) * range_sub on.
@@ -21,14 +23,12 @@ namespace kvq {
 // ------------------------------------------------------------------------------ merge
 
 __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
-  extern __shared__ float sw[];                 // partition weights
-  __shared__ float red[8];
-  __shared__ long long red64[2][8];
+  extern __shared__ float sw[];                 // the streams' partial states
   const int row = blockIdx.x;                   // (b, h, i)
   const int b = row / (a.HQ * a.N);
   const int hi_ = row - b * (a.HQ * a.N);
   const int h = hi_ / a.N, i = hi_ - h * a.N;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int len = max(0, min(a.lengths[b], a.len_cap));
 
   // where partition p of this row lives
@@ -39,9 +39,9 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     mbase = (int64_t)row * a.num_parts * 2;
     obase = (int64_t)row * a.num_parts * a.D;
   } else {
-    // stream: tokens of all sequences before b, and of all sequences
+    // stream: tokens of all sequences before b, and of all sequences (each wave sums them itself)
     long long pre = 0, tot = 0;
-    for (int bb = tid; bb < a.batch; bb += blockDim.x) {
+    for (int bb = lane; bb < a.batch; bb += 64) {
       const long long l = max(0, min(a.lengths[bb], a.len_cap));
       tot += l;
       if (bb < b) pre += l;
@@ -51,10 +51,6 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
       pre += __shfl_xor(pre, off, 64);
       tot += __shfl_xor(tot, off, 64);
     }
-    if (lane == 0) { red64[0][wv] = pre; red64[1][wv] = tot; }
-    __syncthreads();
-    pre = 0; tot = 0;
-    for (int w = 0; w < nw; ++w) { pre += red64[0][w]; tot += red64[1][w]; }
     const int HQG = a.HK * a.qgroups;
     const int64_t T = (int64_t)tot * HQG;
     const int64_t weff = min<int64_t>((int64_t)a.num_ranges, (T + a.min_tokens - 1) / a.min_tokens);
@@ -76,54 +72,50 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     }
   }
 
-  float mx = -INFINITY;
-  for (int p = tid; p < nparts; p += blockDim.x) mx = fmaxf(mx, a.ml[mbase + p * mstride]);
-  mx = block_reduce<OpMax, 1, 64>(mx);
-  if (lane == 0) red[wv] = mx;
-  __syncthreads();
-  float M = -INFINITY;
-  for (int w = 0; w < nw; ++w) M = fmaxf(M, red[w]);
-  __syncthreads();
-
-  float den = 0.0f;
-  for (int p = tid; p < nparts; p += blockDim.x) {
-    const float mp = a.ml[mbase + p * mstride];
-    const float w = (mp == -INFINITY || M == -INFINITY) ? 0.0f : fast_exp2(mp - M);
-    sw[p] = w;
-    den = fmaf(w, a.ml[mbase + p * mstride + 1], den);
-  }
-  den = block_reduce<OpAdd, 1, 64>(den);
-  if (lane == 0) red[wv] = den;
-  __syncthreads();
-  float tot = 0.0f;
-  for (int w = 0; w < nw; ++w) tot += red[w];
-
-  // weighted sum of the partials: thread (stream s, dim lane dl) owns dims 4 dl .. 4 dl + 3 and
-  // partials s, s + S, ...; the S streams' sums are added in LDS
+  // one pass: running (max m, weight sum den, weighted o acc) per thread over its partials
   const int DL = a.D / 4, S = blockDim.x / DL;
   const int dl = tid % DL, sidx = tid / DL;
+  float m_run = -INFINITY, den = 0.0f;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if (sidx < S) {
     const float* ob = a.opart + obase + 4 * dl;
+    const float* mb = a.ml + mbase;
 #pragma unroll 4
     for (int p = sidx; p < nparts; p += S) {
-      const float wp = sw[p];
-      if (wp != 0.0f) {                                  // (a skipped partial's o is never read)
-        const float4 o = *reinterpret_cast<const float4*>(ob + p * ostride);
-        acc.x = fmaf(wp, o.x, acc.x); acc.y = fmaf(wp, o.y, acc.y);
-        acc.z = fmaf(wp, o.z, acc.z); acc.w = fmaf(wp, o.w, acc.w);
-      }
+      const float2 ml = *reinterpret_cast<const float2*>(mb + p * mstride);
+      const float4 o = *reinterpret_cast<const float4*>(ob + p * ostride);
+      // branch-free, so every load is issued ahead of the arithmetic; a skipped partial
+      // (m = -inf) contributes through selects only, so its unwritten l and o are never used
+      const bool ok = ml.x != -INFINITY;
+      const float mnew = ok ? fmaxf(m_run, ml.x) : m_run;
+      const float sc = (mnew == -INFINITY) ? 1.0f : fast_exp2(m_run - mnew);
+      const float wp = ok ? fast_exp2(ml.x - mnew) : 0.0f;
+      m_run = mnew;
+      den = fmaf(den, sc, ok ? wp * ml.y : 0.0f);
+      acc.x = fmaf(acc.x, sc, ok ? wp * o.x : 0.0f); acc.y = fmaf(acc.y, sc, ok ? wp * o.y : 0.0f);
+      acc.z = fmaf(acc.z, sc, ok ? wp * o.z : 0.0f); acc.w = fmaf(acc.w, sc, ok ? wp * o.w : 0.0f);
     }
   }
-  __syncthreads();                                       // sw is reused for the stream sums
+  // the streams' states meet in LDS: [stream][dim lane] float4 acc, then (m, den) per stream
   float4* part = reinterpret_cast<float4*>(sw);
-  if (sidx < S) part[sidx * DL + dl] = acc;
+  float2* mden = reinterpret_cast<float2*>(sw + 4 * S * DL);
+  if (sidx < S) {
+    part[sidx * DL + dl] = acc;
+    if (dl == 0) mden[sidx] = make_float2(m_run, den);
+  }
   __syncthreads();
   if (tid < DL) {
-    float4 r = part[tid];
-    for (int k = 1; k < S; ++k) {
+    float M = -INFINITY;
+    for (int k = 0; k < S; ++k) M = fmaxf(M, mden[k].x);
+    float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float tot = 0.0f;
+    for (int k = 0; k < S; ++k) {
+      const float2 md = mden[k];
+      if (md.x == -INFINITY) continue;
+      const float w = fast_exp2(md.x - M);
       const float4 x = part[k * DL + tid];
-      r.x += x.x; r.y += x.y; r.z += x.z; r.w += x.w;
+      tot = fmaf(w, md.y, tot);
+      r.x = fmaf(w, x.x, r.x); r.y = fmaf(w, x.y, r.y); r.z = fmaf(w, x.z, r.z); r.w = fmaf(w, x.w, r.w);
     }
     const float v[4] = {r.x, r.y, r.z, r.w};
     for (int k = 0; k < 4; ++k) {
@@ -137,9 +129,8 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
 
 hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t s) {
   const unsigned rows = (unsigned)(B * a.HQ * a.N);
-  const int most = a.part_tokens > 0 ? a.num_parts : (a.num_ranges + 1) * a.range_sub;
-  // partition weights, then the 256 threads' float4 sums
-  const size_t shm = (size_t)std::max(most, 256 * 4) * sizeof(float);
+  // the 256 threads' float4 sums and each stream's (max, weight sum)
+  const size_t shm = (size_t)(256 * 4 + 2 * 256) * sizeof(float);
   hipLaunchKernelGGL(merge_kernel, dim3(rows), dim3(256), shm, s, a);
   return hipGetLastError();
 }
