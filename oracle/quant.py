@@ -18,7 +18,13 @@ for 4 bits: scale = (max - min) / 15, bias = min):
 Packing: "@mlx-bun/inference 0.0.0-stage -> 1.0.0", diff page 50, paged.ts
 (``paged_attention_affine_partial``) and kvq4-decode.ts (the partial kernel): element i of
 a row is code ``(word[i / PACK] >> (BITS * (i % PACK))) & (2**BITS - 1)`` with
-PACK = 32 / BITS, i.e. the lowest bits of a word hold its first element.
+PACK = 32 / BITS, i.e. the lowest bits of a word hold its first element.  The same pages
+(diff page 134, paged.ts ``directReadable``) accept widths that do not divide 32 (3, 5 and
+6 bits), whose codes straddle words, but read them only through the library's dequantize and
+never show their layout; the reading here is the plain extension of the rule above: a row's
+codes form one little-endian bit stream, code i in bits [BITS * i, BITS * i + BITS) of the row
+and bit k of the stream in bit k % 32 of word k / 32.  For widths dividing 32 this is the PACK
+rule itself.
 
 Dequantization: value = scale * code + bias, evaluated exactly here in f64 (the
 product of a bf16 and an integer below 256 plus a bf16 is exact in f64); the pages'
@@ -70,23 +76,28 @@ def quantize_codes(x_bits: np.ndarray, bits: int, group: int = GROUP):
 
 
 def pack(codes: np.ndarray, bits: int) -> np.ndarray:
-    """Codes uint32 [..., D] -> words uint32 [..., D * bits / 32], first element in the low bits."""
+    """Codes uint32 [..., D] -> words uint32 [..., D * bits / 32]: the row's codes as one
+    little-endian bit stream (code i in stream bits [bits * i, bits * i + bits), stream bit k
+    in bit k % 32 of word k / 32)."""
     codes = np.asarray(codes, dtype=np.uint32)
-    P = 32 // bits
     D = codes.shape[-1]
-    assert D % P == 0
-    c = codes.reshape(codes.shape[:-1] + (D // P, P))
-    shifts = (np.arange(P, dtype=np.uint32) * np.uint32(bits))
-    return np.bitwise_or.reduce(c << shifts, axis=-1).astype(np.uint32)
+    assert (D * bits) % 32 == 0
+    lead = codes.shape[:-1]
+    # the stream, bit by bit: [..., D, bits], least significant bit of each code first
+    stream = (codes[..., None] >> np.arange(bits, dtype=np.uint32)) & np.uint32(1)
+    stream = stream.reshape(lead + (D * bits // 32, 32))
+    return np.bitwise_or.reduce(stream << np.arange(32, dtype=np.uint32), axis=-1).astype(np.uint32)
 
 
 def unpack(words: np.ndarray, bits: int) -> np.ndarray:
-    """Words uint32 [..., W] -> codes uint32 [..., W * 32 / bits]."""
+    """Words uint32 [..., W] -> codes uint32 [..., W * 32 / bits] (the inverse of pack)."""
     words = np.asarray(words, dtype=np.uint32)
-    P = 32 // bits
-    shifts = (np.arange(P, dtype=np.uint32) * np.uint32(bits))
-    c = (words[..., None] >> shifts) & np.uint32(levels(bits))
-    return c.reshape(words.shape[:-1] + (words.shape[-1] * P,))
+    W = words.shape[-1]
+    assert (W * 32) % bits == 0
+    lead = words.shape[:-1]
+    stream = (words[..., None] >> np.arange(32, dtype=np.uint32)) & np.uint32(1)
+    stream = stream.reshape(lead + (W * 32 // bits, bits))
+    return np.bitwise_or.reduce(stream << np.arange(bits, dtype=np.uint32), axis=-1).astype(np.uint32)
 
 
 def quantize(x_bits: np.ndarray, bits: int, group: int = GROUP):

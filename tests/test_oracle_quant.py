@@ -71,15 +71,40 @@ def test_packing_worked_words():
         assert list(quant.unpack(np.array([[word]], np.uint32), c["bits"])[0]) == c["codes"], c
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [3, 5, 6])
+def test_straddling_widths_pack_as_one_bit_stream(bits):
+    """Widths that do not divide 32: the row's codes as one little-endian bit stream, built
+    here as a Python integer (sum of code_i << (bits * i)) and cut into 32-bit words; a code
+    whose bits cross a word boundary keeps its low bits in the lower word."""
+    rng = np.random.default_rng(100 + bits)
+    for D in (32, 64, 256):
+        codes = rng.integers(0, 1 << bits, size=D)
+        stream = 0
+        for i, c in enumerate(codes):
+            stream |= int(c) << (bits * i)
+        want = [(stream >> (32 * k)) & 0xFFFFFFFF for k in range(D * bits // 32)]
+        got = quant.pack(codes.astype(np.uint32)[None], bits)[0]
+        assert [int(x) for x in got] == want
+        assert np.array_equal(quant.unpack(got[None], bits)[0], codes.astype(np.uint32))
+    # a hand-worked 3-bit row: codes 0..7, 0, 1, 2, ... -> word 0 holds codes 0..9 in bits 0..29
+    # and the low two bits of code 10 (= 2, binary 10) in bits 30..31
+    if bits == 3:
+        codes = (np.arange(32) % 8).astype(np.uint32)[None]
+        w0 = sum(c << (3 * i) for i, c in enumerate([0, 1, 2, 3, 4, 5, 6, 7, 0, 1])) | (2 << 30)
+        assert int(quant.pack(codes, 3)[0, 0]) == w0 == 0x88FAC688
+        assert int(quant.pack(codes, 3)[0, 1]) == (2 >> 2) | (3 << 1) | (4 << 4) | (5 << 7) | (6 << 10) | (
+            7 << 13) | (0 << 16) | (1 << 19) | (2 << 22) | (3 << 25) | (4 << 28) | ((5 & 1) << 31)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 def test_pack_unpack_round_trip(bits):
     rng = np.random.default_rng(bits)
     codes = rng.integers(0, 1 << bits, size=(7, 3, 256)).astype(np.uint32)
     words = quant.pack(codes, bits)
     assert words.shape == (7, 3, 256 * bits // 32)
     assert np.array_equal(quant.unpack(words, bits), codes)
-    # and the other way round: any word survives unpack -> pack
-    w = rng.integers(0, 1 << 32, size=(5, 8), dtype=np.uint64).astype(np.uint32)
+    # and the other way round: any word survives unpack -> pack (rows of whole codes)
+    w = rng.integers(0, 1 << 32, size=(5, 8 * bits), dtype=np.uint64).astype(np.uint32)
     assert np.array_equal(quant.pack(quant.unpack(w, bits), bits), w)
 
 
@@ -139,7 +164,7 @@ def _half_even(fr: Fraction) -> int:
     return fl
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 def test_quantizer_against_exact_rationals(bits):
     """Brute force in exact arithmetic: scale is the smallest bf16 >= RN32((max-min)/n), and each
     code is round-half-even of the exact quotient, except where the exact quotient lies within
@@ -166,13 +191,13 @@ def test_quantizer_against_exact_rationals(bits):
                 assert int(codes[r, d]) == want, (r, d, float(qx))
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("wl", ["c3", "c5", "c2"])
 @pytest.mark.parametrize("group", [64, 32, 128])
 def test_quantize_error_bound(bits, wl, group):
     """|x - dequant(quant(x))| <= scale / 2 for every element; codes within [0, 2^bits - 1];
     the group minimum maps to code 0 and the maximum to the top code (bits <= 4) or within
-    2 of it (8 bits, where the rounded-up scale can leave the top code unused)."""
+    2 of it (5, 6 and 8 bits, where the rounded-up scale can leave the top code unused)."""
     w = make_workload(wl, B=2, len_lo=300, len_hi=400, D=256, HK=2)
     k, v = w.kv(0)
     for x in (k, v):
@@ -195,7 +220,7 @@ def test_quantize_error_bound(bits, wl, group):
             assert np.all(top >= n - 2)
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 def test_group_size_is_a_partition_of_the_row(bits):
     """Scale groups are independent: quantizing a row with groups of G equals quantizing each
     G-element slice as a one-group row (checked for G = 32, 64, 128 against G = slice length), and
