@@ -226,7 +226,8 @@ def kv_gather_debug(pool: "Pool", block_table, lengths, batch: int, max_blocks: 
 class Pool:
     """A block pool whose planes are torch device tensors wrapped by the library.
 
-    planes["k"], planes["v"]: uint32 codes [NB, HK, BS, D*bits/32] (affine) or bf16 bit
+    planes["k"], planes["v"]: uint32 codes [NB, HK, BS, D*bits/32] (affine; a row's codes are one
+    little-endian bit stream, so 3/5/6-bit codes straddle words) or bf16 bit
     patterns as int16 [NB, HK, BS, D] (bits == 16); planes["{k,v}_{scale,bias}"]: bf16
     bit patterns as int16 [NB, HK, BS, D/64].
     """

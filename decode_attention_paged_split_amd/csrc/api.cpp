@@ -48,10 +48,14 @@ int validate_desc(const kvq_pool_desc* d) {
   if (d->num_blocks < 1 || d->num_kv_heads < 1 || d->block_size < 1 || d->head_dim < 1)
     return fail(KVQ_ERR_INVALID, "pool sizes must be positive (NB=%d HK=%d BS=%d D=%d)",
                 d->num_blocks, d->num_kv_heads, d->block_size, d->head_dim);
-  if (!(d->bits == 16 || d->bits == 8 || d->bits == 4 || d->bits == 2))
-    return fail(KVQ_ERR_UNSUPPORTED, "bits must be 16 (bf16 pages) or 8, 4, 2 (affine), got %d", d->bits);
+  if (!(d->bits == 16 || d->bits == 8 || d->bits == 6 || d->bits == 5 || d->bits == 4 || d->bits == 3 ||
+        d->bits == 2))
+    return fail(KVQ_ERR_UNSUPPORTED, "bits must be 16 (bf16 pages) or 8, 6, 5, 4, 3, 2 (affine), got %d", d->bits);
   if (d->head_dim % 64 != 0 || d->head_dim > 256)
     return fail(KVQ_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256, got %d", d->head_dim);
+  if (!kvq::valu_row_ok(d->bits, d->head_dim))
+    return fail(KVQ_ERR_UNSUPPORTED, "a %d-bit row of %d dims is %d bytes; rows must be whole 16-byte chunks",
+                d->bits, d->head_dim, d->head_dim * d->bits / 8);
   if (!(d->group_size == 32 || d->group_size == 64 || d->group_size == 128) || d->head_dim % d->group_size != 0)
     return fail(KVQ_ERR_UNSUPPORTED, "group_size must be 32, 64 or 128 and divide head_dim, got %d", d->group_size);
   const size_t rows = (size_t)d->num_blocks * d->num_kv_heads * d->block_size;

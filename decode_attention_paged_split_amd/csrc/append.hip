@@ -34,7 +34,10 @@ hipError_t launch_append(const AppendArgs& a, int bits, hipStream_t stream) {
   switch (bits) {
     case 16: return launch_append_g<16>(a, g, stream);
     case 8: return launch_append_g<8>(a, g, stream);
+    case 6: return launch_append_g<6>(a, g, stream);
+    case 5: return launch_append_g<5>(a, g, stream);
     case 4: return launch_append_g<4>(a, g, stream);
+    case 3: return launch_append_g<3>(a, g, stream);
     case 2: return launch_append_g<2>(a, g, stream);
     default: return hipErrorInvalidValue;
   }

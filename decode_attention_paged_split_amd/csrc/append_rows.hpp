@@ -15,13 +15,16 @@
 //   mn, mx = min, max of the group;  scale = bf16_round_up(f32(mx - mn) / (2^bits - 1));
 //   bias = mn (a zero minimum stored as +0);
 //   code = clamp(rint(f32(x - bias) / scale), 0, 2^bits - 1), rint = half to even,
-//   code 0 everywhere when scale == 0;  codes packed low-first into uint32 words.
+//   code 0 everywhere when scale == 0.
 // Division is IEEE round-to-nearest (__fdiv_rn), never a reciprocal approximation, so
 // codes match any correctly rounded f32 implementation exactly.
 //
-// Mapping: one thread per EPT consecutive elements of one (token, head) row (EPT = 8,
-// or 16 at 2 bits so that a thread owns whole words); the GS/EPT threads of a group are
-// adjacent lanes and reduce min/max with DPP.  Loads are 16-byte, coalesced along the row.
+// Packing: a row's codes form one little-endian bit stream, code i in bits [bits * i, bits * i +
+// bits) (the pages' low-first rule; 3-, 5- and 6-bit codes straddle words).
+// Mapping: one thread per EPT consecutive elements of one (token, head) row (EPT = 8, 16 at 2
+// bits and 32 at 3, 5 and 6 bits, so that a thread owns whole words); the GS/EPT threads of a
+// group are adjacent lanes and reduce min/max with DPP.  Loads are 16-byte, coalesced along
+// the row.
 #pragma once
 
 #include "device_common.hpp"
@@ -29,7 +32,7 @@
 
 namespace kvq {
 
-constexpr int append_ept(int bits) { return bits == 2 ? 16 : 8; }
+constexpr int append_ept(int bits) { return bits == 2 ? 16 : (32 % bits != 0 ? 32 : 8); }
 
 // slot of new row tok = b * N + i of a decode step: position lengths[b] - N + i looked up in the
 // block table; -1 (skipped) when the position is outside [0, capacity) or the entry is outside the pool
@@ -67,13 +70,10 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int64_t gid) {
     const uint16_t* src = kv ? a.v : a.k;
     const uint4* s4 = reinterpret_cast<const uint4*>(src + row * a.D + chunk * EPT);
     uint32_t w[EPT / 2];
-    {
-      uint4 x0 = live ? s4[0] : make_uint4(0, 0, 0, 0);
-      w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
-      if constexpr (EPT == 16) {
-        uint4 x1 = live ? s4[1] : make_uint4(0, 0, 0, 0);
-        w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
-      }
+#pragma unroll
+    for (int q = 0; q < EPT / 8; ++q) {
+      const uint4 x = live ? s4[q] : make_uint4(0, 0, 0, 0);
+      w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
     }
     if constexpr (BITS == 16) {
       if (store) {
@@ -107,15 +107,16 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int64_t gid) {
         q = fminf(fmaxf(q, 0.0f), NLEV);
         c[i] = (uint32_t)q;
       }
-      constexpr int PACK = 32 / BITS;
-      constexpr int NWORDS = EPT / PACK;
+      // the thread's codes as its stretch of the row's bit stream (EPT * BITS bits, whole words)
+      constexpr int NWORDS = EPT * BITS / 32;
       uint32_t out[NWORDS];
 #pragma unroll
-      for (int j = 0; j < NWORDS; ++j) {
-        uint32_t acc = 0;
+      for (int j = 0; j < NWORDS; ++j) out[j] = 0;
 #pragma unroll
-        for (int i = 0; i < PACK; ++i) acc |= c[j * PACK + i] << (BITS * i);
-        out[j] = acc;
+      for (int i = 0; i < EPT; ++i) {
+        const int o = BITS * i, wj = o >> 5, sh = o & 31;
+        out[wj] |= c[i] << sh;
+        if (sh + BITS > 32) out[wj + 1] |= c[i] >> (32 - sh);   // a code straddling two words
       }
       if (store) {
         const int W = a.D * BITS / 32;

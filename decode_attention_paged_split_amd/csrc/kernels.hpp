@@ -88,11 +88,13 @@ hipError_t launch_step_prep(const AppendArgs& ap, const PartialArgs& a, int bits
                             bool vector_q, int B, hipStream_t stream);
 bool partial_supported(int bits, int D, int gs, int qvw);
 // most query vectors one wave of the vector engine carries: 8, or 4 where a V lane owns 16 head
-// dims (2-bit pages; bf16 and 8-bit pages at head dim 256) or a row has 8 scale groups (the
-// per-lane bias sums, vectors x groups, stay within 32 registers)
+// dims (2-bit pages; bf16, 8-, 6- and 5-bit pages at head dim 256, whose rows take two parts) or
+// a row has 8 scale groups (the per-lane bias sums, vectors x groups, stay within 32 registers)
 constexpr int valu_max_qvw(int bits, int D, int gs) {
-  return (bits == 2 || (D == 256 && bits >= 8) || (bits != 16 && D / gs > 4)) ? 4 : 8;
+  return (bits == 2 || (D == 256 && bits >= 5) || (bits != 16 && D / gs > 4)) ? 4 : 8;
 }
+// a row layout the vector engine reads: whole 16-byte chunks
+constexpr bool valu_row_ok(int bits, int D) { return (D * bits / 8) % 16 == 0; }
 
 // matrix-core engine (4-bit pages, head dim 128/256, stream schedule, 16 query vectors per wave,
 // 64-token tiles)

@@ -1,0 +1,7 @@
+// Vector-engine kernels for 3-bit pages, whose codes straddle words (one translation unit per page format keeps the build parallel).
+#include "partial_valu_impl.hpp"
+
+namespace kvq {
+template hipError_t launch_valu_bits<3>(const PartialArgs&, int, int, int, int, bool, hipStream_t);
+template hipError_t launch_step_bits<3>(const AppendArgs&, const PartialArgs&, int, int, int, bool, int, hipStream_t);
+}  // namespace kvq

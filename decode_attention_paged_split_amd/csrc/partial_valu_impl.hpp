@@ -68,26 +68,30 @@ template <int BITS, int D, int GS>
 struct Geo {
   static constexpr int ROWB = D * BITS / 8;                 // bytes per pool row
   static constexpr bool AFF = BITS != 16;
+  static constexpr bool STR = AFF && (32 % BITS != 0);      // codes straddle words (3, 5, 6 bits)
   static constexpr int GSZ = AFF ? GS : 64;                 // dims per scale group (bf16: 64-dim blocks)
   static constexpr int G = D / GSZ;                         // scale groups per row
-  static constexpr int KPB = ROWB < 128 ? ROWB : 128;       // bytes of a row per part
-  static constexpr int NP = ROWB / KPB;                     // parts per row
+  static constexpr int NP = (ROWB + 127) / 128;             // parts per row (<= 128 bytes each)
+  static constexpr int KPB = ROWB / NP;                     // bytes of a row per part
   static constexpr int KCP = KPB / 16;                      // 16-byte chunks per part
   static constexpr int GPP = G / NP;                        // scale groups per part
   static constexpr int NHB = GSZ / 32;                      // 16-pair blocks per group
-  static constexpr int PPW = (BITS == 16) ? 1 : 16 / BITS;  // bf16 pairs per word
-  static constexpr int WPH = 16 / PPW;                      // words per 16-pair block
+  static constexpr int WPH = BITS;                          // words per 16-pair block (32 dims)
+  static constexpr int PPW = STR ? 0 : (BITS == 16 ? 1 : 16 / BITS);  // bf16 pairs per word
   static constexpr int DPP_ = KPB * 8 / BITS;               // head dims per part
-  static constexpr int VW = (BITS == 16) ? 8 : 4;           // V bytes per lane per row
+  // V bytes per lane per row: 8 dims (straddling widths: 8 codes = BITS bytes, read as two
+  // dwords and shifted into place), 4 dims (bf16) or one dword of codes
+  static constexpr int VW = STR ? BITS : (BITS == 16 ? 8 : 4);
   static constexpr int VLPR = KPB / VW;                     // V lanes per row (one part)
   static constexpr int VRPL = 64 / VLPR;                    // rows per V read
   static constexpr int VDPL = VW * 8 / BITS;                // dims per V lane per part
   static constexpr int NBV = PV_TILE / VRPL;                // V reads per part
   static constexpr int VPITCH = KPB + 16;                   // LDS pitch of a staged V row
   static constexpr int WG = AFF ? G : 1;                    // weights per (token, vector)
-  static constexpr float OFFS = (BITS == 4 || BITS == 2) ? 128.0f : 0.0f;
+  static constexpr float OFFS = (AFF && BITS <= 6) ? 128.0f : 0.0f;   // K codes as bf16(128 + c)
+  static_assert(ROWB % NP == 0 && KPB % 16 == 0, "rows of whole 16-byte chunks per part");
   static_assert(G % NP == 0 && GPP * NHB * WPH * 4 == KPB, "whole groups per part");
-  static_assert(VLPR >= 1 && VLPR <= 64 && GSZ % VDPL == 0, "V layout");
+  static_assert(VLPR >= 1 && VLPR <= 64 && 64 % VLPR == 0 && KPB % VW == 0 && GSZ % VDPL == 0, "V layout");
 };
 
 // dims (lo, hi) of bf16 pair P in the codes' order (natural word order; inside a word the
@@ -129,6 +133,42 @@ __device__ __forceinline__ void word_pairs(uint32_t w, uint32_t* out, uint32_t m
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) out[k] = and_or(w >> (2 * k), 0x00030003u, magic);
+  }
+}
+
+// the 32 codes of a 16-pair block of a straddling-width row (BITS words, one little-endian bit
+// stream) -> 16 bf16 pairs (dims 2p, 2p + 1) as bf16(128 + c), exact: the pair's 2 * BITS bits are
+// funnel-shifted down (v_alignbit_b32 where they cross a word), the low code masked into the
+// low half and the high code shifted and masked into the high half
+template <int BITS>
+__device__ __forceinline__ void block_pairs(const uint32_t* w, uint32_t* out, uint32_t magic) {
+  constexpr uint32_t M = (1u << BITS) - 1u;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    constexpr int F = 2 * BITS;
+    const int o = F * p, wj = o >> 5, sh = o & 31;
+    uint32_t x;
+    if (sh + F <= 32) x = sh ? (w[wj] >> sh) : w[wj];
+    else x = __builtin_amdgcn_alignbit(w[wj + 1], w[wj], sh);
+    out[p] = and_or(x << (16 - BITS), M << 16, and_or(x, M, magic));
+  }
+}
+
+// the 8 codes of a straddling-width V lane -> f32: (w0, w1) are the two dwords from the lane's
+// first byte rounded down to a dword, s = 8 * (that byte offset % 4); the codes sit at bits
+// BITS * d of the 64-bit value (w1:w0) >> s (8 * BITS + s <= 64 for every lane of a row)
+template <int BITS>
+__device__ __forceinline__ void value8_str(uint32_t w0, uint32_t w1, uint32_t s, float* v) {
+  const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, s);
+  const uint32_t hi = w1 >> s;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    const int o = BITS * d;
+    uint32_t c;
+    if (o + BITS <= 32) c = __builtin_amdgcn_ubfe(lo, o, BITS);
+    else if (o >= 32) c = __builtin_amdgcn_ubfe(hi, o - 32, BITS);
+    else c = __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(hi, lo, o), 0, BITS);
+    v[d] = (float)c;
   }
 }
 
@@ -401,10 +441,20 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
           uint32_t kp[16];
+          if constexpr (Gm::STR) {
+            uint32_t bw[WPH];
 #pragma unroll
-          for (int wi = 0; wi < WPH; ++wi) {
-            const int word = (gp * NHB + hb) * WPH + wi;          // word of the part
-            word_pairs<BITS>(kpart.c[word >> 2][word & 3], &kp[wi * PPW], magic);
+            for (int wi = 0; wi < WPH; ++wi) {
+              const int word = (gp * NHB + hb) * WPH + wi;        // word of the part
+              bw[wi] = kpart.c[word >> 2][word & 3];
+            }
+            block_pairs<BITS>(bw, kp, magic);
+          } else {
+#pragma unroll
+            for (int wi = 0; wi < WPH; ++wi) {
+              const int word = (gp * NHB + hb) * WPH + wi;        // word of the part
+              word_pairs<BITS>(kpart.c[word >> 2][word & 3], &kp[wi * PPW], magic);
+            }
           }
 #pragma unroll
           for (int j = 0; j < QVW; ++j) {
@@ -499,15 +549,21 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
 #pragma unroll
           for (int j = 0; j < QVW; ++j) wv[j] = ws.wrow(r, vgrp)[j];
         }
-        uint32_t cw[VW / 4];
-        if constexpr (VW == 8) {
-          const uint2 x = *reinterpret_cast<const uint2*>(&ws.v[r][vsl * VW]);
-          cw[0] = x.x; cw[1] = x.y;
-        } else {
-          cw[0] = *reinterpret_cast<const uint32_t*>(&ws.v[r][vsl * VW]);
-        }
         float vv[VDPL];
-        value_f32<BITS, VDPL>(cw, vv);
+        if constexpr (Gm::STR) {
+          const int ob = vsl * VW;                                // the lane's first byte
+          const uint32_t* src = reinterpret_cast<const uint32_t*>(&ws.v[r][ob & ~3]);
+          value8_str<BITS>(src[0], src[1], 8u * (uint32_t)(ob & 3), vv);
+        } else {
+          uint32_t cw[VW / 4];
+          if constexpr (VW == 8) {
+            const uint2 x = *reinterpret_cast<const uint2*>(&ws.v[r][vsl * VW]);
+            cw[0] = x.x; cw[1] = x.y;
+          } else {
+            cw[0] = *reinterpret_cast<const uint32_t*>(&ws.v[r][vsl * VW]);
+          }
+          value_f32<BITS, VDPL>(cw, vv);
+        }
 #pragma unroll
         for (int j = 0; j < QVW; ++j)
 #pragma unroll
@@ -872,7 +928,9 @@ static hipError_t with_group(int gs, int qvw, F f) {
 template <int BITS, class F>
 static hipError_t with_shape(int D, int gs, int qvw, F f) {
   switch (D) {
-    case 64: return with_group<BITS, 64>(gs, qvw, f);
+    case 64:
+      if constexpr (valu_row_ok(BITS, 64)) return with_group<BITS, 64>(gs, qvw, f);
+      return hipErrorInvalidValue;
     case 128: return with_group<BITS, 128>(gs, qvw, f);
     case 256: return with_group<BITS, 256>(gs, qvw, f);
     default: return hipErrorInvalidValue;

@@ -44,10 +44,13 @@ typedef enum kvq_status {
 
 /* Pool planes, each shaped [num_blocks, num_kv_heads, block_size, width] ([P134]
  * cache.ts, class BlockPool).  bf16 pages (bits == 16) have only K and V (uint16, width
- * head_dim).  Affine pages have packed codes K and V (uint32, width head_dim*bits/32,
- * element i of a row in bits [bits*(i%P), bits*(i%P+1)) of word i/P, P = 32/bits:
- * [P50] paged.ts, paged_attention_affine_partial) and bf16 scale and bias planes of
- * width head_dim/group_size. */
+ * head_dim).  Affine pages have packed codes K and V (uint32, width head_dim*bits/32) and
+ * bf16 scale and bias planes of width head_dim/group_size.  A row's codes are one
+ * little-endian bit stream: element i in stream bits [bits*i, bits*i + bits), stream bit k in
+ * bit k%32 of word k/32.  For widths dividing 32 that is bits [bits*(i%P), bits*(i%P+1)) of
+ * word i/P, P = 32/bits ([P50] paged.ts, paged_attention_affine_partial); 3-, 5- and 6-bit
+ * codes straddle words ([P134] paged.ts, directReadable, names such widths but reads them
+ * only through the library's dequantize, so their layout is this build's reading). */
 typedef enum kvq_plane {
   KVQ_PLANE_K = 0,
   KVQ_PLANE_V = 1,
@@ -63,8 +66,9 @@ typedef struct kvq_pool_desc {
   int32_t num_kv_heads;  /* HK >= 1 */
   int32_t block_size;    /* tokens per block BS >= 1 */
   int32_t head_dim;      /* D, a multiple of group_size, at most 256 */
-  int32_t bits;          /* 16 = bf16 pages; 8, 4 or 2 = affine codes (32 % bits == 0) */
-  int32_t group_size;    /* elements per scale/bias group along the head dim: 64 */
+  int32_t bits;          /* 16 = bf16 pages; 8, 6, 5, 4, 3 or 2 = affine codes; a row of codes
+                            (head_dim*bits/8 bytes) must be whole 16-byte chunks */
+  int32_t group_size;    /* elements per scale/bias group along the head dim: 32, 64 or 128 */
 } kvq_pool_desc;
 
 typedef struct kvq_pool kvq_pool;  /* opaque */

@@ -65,7 +65,7 @@ def test_pool_bytes_match_the_layout(lib, name, expect):
         assert kvq.kv_pool_plane_bytes(d, 5) == rows * (w.D // 64) * 2
 
 
-@pytest.mark.parametrize("field,value,code", [("bits", 3, -2), ("bits", 32, -2), ("group_size", 48, -2),
+@pytest.mark.parametrize("field,value,code", [("bits", 7, -2), ("bits", 1, -2), ("bits", 32, -2), ("group_size", 48, -2),
                                               ("group_size", 256, -2), ("group_size", 16, -2),
                                               ("head_dim", 96, -2), ("head_dim", 512, -2),
                                               ("num_blocks", 0, -1), ("block_size", 0, -1)])
@@ -85,6 +85,23 @@ def test_group_sizes(lib, group, D, ok):
     if ok:
         h = kvq.kv_pool_wrap(d, [16] * 6)
         assert kvq.kv_pool_plane_bytes(d, 3) == 4 * 2 * 16 * (D // group) * 2
+        kvq.kv_pool_destroy(h)
+    else:
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kv_pool_wrap(d, [16] * 6)
+        assert e.value.code == -2
+
+
+@pytest.mark.parametrize("bits,D,ok", [(3, 128, True), (3, 256, True), (5, 128, True), (5, 256, True),
+                                        (6, 64, True), (6, 256, True), (3, 64, False), (5, 64, False)])
+def test_straddling_widths(lib, bits, D, ok):
+    """3/5/6-bit pages: the codes plane holds D * bits / 8 bytes per row (one bit stream); a row
+    must be whole 16-byte chunks (head dim 64 at 3 or 5 bits is not: 24 or 40 bytes)."""
+    d = kvq.PoolDesc(4, 2, 16, D, bits, 32)
+    if ok:
+        h = kvq.kv_pool_wrap(d, [16] * 6)
+        assert kvq.kv_pool_plane_bytes(d, 0) == 4 * 2 * 16 * D * bits // 8
+        assert kvq.kv_pool_plane_bytes(d, 5) == 4 * 2 * 16 * (D // 32) * 2
         kvq.kv_pool_destroy(h)
     else:
         with pytest.raises(kvq.KvqError) as e:
