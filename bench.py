@@ -22,6 +22,7 @@ a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import concurrent.futures
 import hashlib
 import json
 import os
@@ -122,11 +123,15 @@ def main():
     ap.add_argument("--engine", choices=["auto", "vector", "matrix"], default="auto",
                     help="partial-pass engine: vector ALU (the default) or matrix cores (4-bit pages)")
     ap.add_argument("--cold", action="store_true", help="write 1 GiB before each step (defeats the caches)")
+    ap.add_argument("--also-cold", action="store_true",
+                    help="after the warm steps, time as many cold ones and add them to the record")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--probe-copy", type=int, default=0, metavar="BYTES",
                     help="instead: time a plain device copy of BYTES (achievable-bandwidth probe, and the "
                          "known-size kernel that calibrates the HBM byte counters)")
+    ap.add_argument("--probe-read", type=int, default=0, metavar="BYTES",
+                    help="instead: time a streaming read of BYTES (achievable read bandwidth)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -143,6 +148,24 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.probe_read:
+        # achievable streaming-read rate: a sum over BYTES of f32 (reads BYTES, writes one value)
+        src = torch.ones(args.probe_read // 4, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            acc = src.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            acc = src.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"probe": "read (torch.sum)", "bytes_read": src.numel() * 4,
+                          "us_per_read": round(ms * 1e3, 2),
+                          "GB_per_s": round(src.numel() * 4 / (ms * 1e-3) / 1e9, 1)}))
+        return
 
     if args.probe_copy:
         src = torch.ones(args.probe_copy // 4, dtype=torch.float32, device=dev)
@@ -168,8 +191,16 @@ def main():
         f"BS={w.BS} sum(len)={int(w.lengths.sum())} NB={w.num_blocks}")
     pool = kvq.Pool(w.num_blocks, w.HK, w.BS, w.D, w.bits, device=dev)
     new_k, new_v, new_slots = [], [], []
+    # the draws of each sequence are independent (own seed), so a few threads generate them
+    # ahead of the device appends (NumPy's generators release the GIL)
+    gen = concurrent.futures.ThreadPoolExecutor(max_workers=8)
+    ahead = 16
+    futs = [gen.submit(w.kv, b) for b in range(min(ahead, w.B))]
     for b in range(w.B):
-        k, v = w.kv(b)
+        k, v = futs[b].result()
+        futs[b] = None
+        if b + ahead < w.B:
+            futs.append(gen.submit(w.kv, b + ahead))
         L = int(w.lengths[b])
         pool.append(torch.from_numpy(k[: L - w.N].view(np.int16)).to(dev),
                     torch.from_numpy(v[: L - w.N].view(np.int16)).to(dev),
@@ -177,6 +208,7 @@ def main():
         new_k.append(k[L - w.N:]), new_v.append(v[L - w.N:]), new_slots.append(w.slots(b, L - w.N, L))
         if b % 8 == 7:
             log(f"[bench] filled {b + 1}/{w.B} sequences ({time.time() - t_setup:.0f} s)")
+    gen.shutdown()
     nk = torch.from_numpy(np.concatenate(new_k).view(np.int16)).to(dev)
     nv = torch.from_numpy(np.concatenate(new_v).view(np.int16)).to(dev)
     ns = torch.from_numpy(np.concatenate(new_slots)).to(dev)
@@ -210,38 +242,71 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
 
-    # two events per step: after the partial pass and after the merge (the previous step's end,
-    # or the start event, opens the next step)
-    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    ev0 = E()
-    mids = [E() for _ in range(args.steps)]
-    ends = [E() for _ in range(args.steps)]
-    starts = [E() for _ in range(args.steps)] if flush is not None else None
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for i in range(args.steps):
-        if flush is not None:
-            flush.fill_(1)
-            starts[i].record()
-        step(mids[i])
-        ends[i].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    opens = starts if starts is not None else [ev0] + ends[:-1]
-    par = [o.elapsed_time(m) for o, m in zip(opens, mids)]
-    mer = [m.elapsed_time(e) for m, e in zip(mids, ends)]
-    tot = [o.elapsed_time(e) for o, e in zip(opens, ends)]
-    ms_step = float(np.mean(tot)) if args.cold else ev0.elapsed_time(ends[-1]) / args.steps
-    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (append + q copy + partial "
-        f"{np.mean(par) * 1e3:.1f}, merge {np.mean(mer) * 1e3:.1f}); wall {wall:.3f} s")
+    def timed(nsteps, flush_buf, shp=shape, wsp=ws):
+        """nsteps timed steps, then as many again under the library's launch timing.  Torch events
+        per step: after the partial pass and after the merge (warm: the previous step's end, or
+        the start event, opens the next step; cold: an event after the 1 GiB write).  The launch
+        timing brackets each kernel with events on its own stream; those event records add a few
+        microseconds between kernels, so the step time comes from the first pass and only the
+        kernel durations from the second.  Returns a dict: ms per step, partial-pass and merge ms
+        lists, wall s, and the mean ms of the prep, partial and merge kernels."""
+        E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        ev0 = E()
+        mids = [E() for _ in range(nsteps)]
+        ends = [E() for _ in range(nsteps)]
+        starts = [E() for _ in range(nsteps)] if flush_buf is not None else None
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record()
+        for i in range(nsteps):
+            if flush_buf is not None:
+                flush_buf.fill_(1)
+                starts[i].record()
+            step(mids[i], shp, wsp)
+            ends[i].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kvq.kvq_timing_enable(True)
+        for i in range(nsteps):
+            if flush_buf is not None:
+                flush_buf.fill_(1)
+            step(None, shp, wsp)
+        torch.cuda.synchronize()
+        kern = {k: kvq.kvq_timing_read(v)[0] for k, v in
+                (("prep", kvq.TIMING_PREP), ("partial", kvq.TIMING_PARTIAL), ("merge", kvq.TIMING_MERGE))}
+        kvq.kvq_timing_enable(False)
+        opens = starts if starts is not None else [ev0] + ends[:-1]
+        par = [o.elapsed_time(m) for o, m in zip(opens, mids)]
+        mer = [m.elapsed_time(e) for m, e in zip(mids, ends)]
+        tot = [o.elapsed_time(e) for o, e in zip(opens, ends)]
+        ms = float(np.mean(tot)) if flush_buf is not None else ev0.elapsed_time(ends[-1]) / nsteps
+        return {"ms": ms, "par": par, "mer": mer, "wall": wall, "kern": kern}
 
+    t = timed(args.steps, flush)
+    ms_step, par, mer, wall = t["ms"], t["par"], t["mer"], t["wall"]
+    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (append + q copy + partial "
+        f"{np.mean(par) * 1e3:.1f}, merge {np.mean(mer) * 1e3:.1f}); kernels (library events): prep "
+        f"{t['kern']['prep'] * 1e3:.1f}, partial {t['kern']['partial'] * 1e3:.1f}, merge "
+        f"{t['kern']['merge'] * 1e3:.1f} us; wall {wall:.3f} s")
     eff = w.effective_bytes()
+    cold_rec = None
+    if args.also_cold and not args.cold:
+        fl = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        tc = timed(args.steps, fl)
+        del fl
+        cold_rec = {"us_per_step": round(tc["ms"] * 1e3, 2),
+                    "GB_per_s": round(eff / (tc["ms"] * 1e-3) / 1e9, 1),
+                    "partial_pass_us": round(float(np.mean(tc["par"])) * 1e3, 2),
+                    "partial_kernel_us": round(tc["kern"]["partial"] * 1e3, 2),
+                    "merge_us": round(float(np.mean(tc["mer"])) * 1e3, 2),
+                    "note": "1 GiB written before each step (more than the 256 MB Infinity Cache)"}
+        log(f"[bench] cold: {tc['ms'] * 1e3:.1f} us/step")
+
     gbs = eff / (ms_step * 1e-3) / 1e9
-    part_s = float(np.mean(par)) * 1e-3
+    part_s = t["kern"]["partial"] * 1e-3                   # the partial kernel alone
     achieved = eff / part_s / 1e9
     src_hash = kernel_source_hash() if args.engine != "matrix" else None
-    # binding roof of the partial pass: HBM (effective bytes / 8 TB/s) or the vector ALU
+    # binding roof of the partial kernel: HBM (effective bytes / 8 TB/s) or the vector ALU
     # (2 * REP * N * D multiply-adds per cached token and KV head / the fp32 vector peak)
     flops = w.attention_flops()
     hbm_floor = eff / (HBM_PEAK_GBS * 1e9)
@@ -254,8 +319,7 @@ def main():
     roof = {"bound": "alu" if top is alu else "hbm", "achieved": top["achieved"], "peak": top["peak"],
             "unit": top["unit"], "frac": top["frac"],
             "traffic": traffic_from_profiles(w.name, src_hash) if src_hash else None,
-            "kernel": "partial pass: append of the step's rows + q copy + partial kernel "
-                      "(events around paged_decode_step_partial)",
+            "kernel": "partial kernel (library launch events on its stream, mean over the timed steps)",
             "kernel_us": round(part_s * 1e6, 2),
             "algorithmic_bytes_per_launch": eff, "algorithmic_flops_per_launch": flops,
             "hbm": hbm, "alu": alu, "kernel_source_hash": src_hash}
@@ -267,26 +331,18 @@ def main():
         ws_m = torch.empty(kvq.paged_decode_workspace_bytes(pool, shp_m), dtype=torch.uint8, device=dev)
         for _ in range(3):
             step(None, shp_m, ws_m)
-        e0m = E()
-        midm = [E() for _ in range(args.steps)]
-        endm = [E() for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        e0m.record()
-        for i in range(args.steps):
-            step(midm[i], shp_m, ws_m)
-            endm[i].record()
-        torch.cuda.synchronize()
-        ms_m = e0m.elapsed_time(endm[-1]) / args.steps
-        par_m = float(np.mean([o.elapsed_time(m) for o, m in zip([e0m] + endm[:-1], midm)]))
+        tm = timed(args.steps, None, shp_m, ws_m)
+        ms_m, km = tm["ms"], tm["kern"]["partial"]
         variants["matrix_engine"] = {
             "value": round(eff / (ms_m * 1e-3) / 1e9, 1), "unit": "GB/s", "us_per_step": round(ms_m * 1e3, 2),
             "pct_hbm_peak": round(100 * eff / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-            "partial_us": round(par_m * 1e3, 2),
-            "roofline": {"bound": "hbm", "achieved": round(eff / (par_m * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(eff / (par_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "mfma_tflops": round(flops / (par_m * 1e-3) / 1e12, 2)},
+            "partial_kernel_us": round(km * 1e3, 2),
+            "kernels_us": {k: round(v * 1e3, 2) for k, v in tm["kern"].items()},
+            "roofline": {"bound": "hbm", "achieved": round(eff / (km * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(eff / (km * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "mfma_tflops": round(flops / (km * 1e-3) / 1e12, 2)},
             "note": "engine=2: MFMA q.k and P.V, 4-bit pages; not the default path"}
-        log(f"[bench] matrix engine: {ms_m * 1e3:.1f} us/step (partial {par_m * 1e3:.1f})")
+        log(f"[bench] matrix engine: {ms_m * 1e3:.1f} us/step (partial kernel {km * 1e3:.1f})")
     rec = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
@@ -298,11 +354,14 @@ def main():
                    "partition_tokens": pt, "cold": bool(args.cold), "engine": args.engine},
         "us_per_step": round(ms_step * 1e3, 2), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "effective_bytes": eff,
-        "kernels_us": {"append_qcopy_partial": round(part_s * 1e6, 2), "merge": round(float(np.mean(mer)) * 1e3, 2)},
+        "kernels_us": {k: round(v * 1e3, 2) for k, v in t["kern"].items()},
+        "partial_pass_us": round(float(np.mean(par)) * 1e3, 2),
         "roofline": roof,
     }
     if variants:
         rec["variants"] = variants
+    if cold_rec is not None:
+        rec["cold"] = cold_rec
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

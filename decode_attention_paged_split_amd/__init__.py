@@ -28,10 +28,12 @@ __all__ = [
     "kv_pool_destroy", "kv_pool_plane_bytes", "kv_append_quantize", "paged_decode_workspace_bytes",
     "paged_decode_partition_tokens", "paged_decode_attention", "paged_decode_partial",
     "paged_decode_merge", "paged_decode_step", "paged_decode_step_partial", "kv_gather_debug", "make_shape", "gather", "decode_step",
+    "kvq_timing_enable", "kvq_timing_read", "TIMING_PREP", "TIMING_PARTIAL", "TIMING_MERGE",
     "PLANES", "LIB_PATH",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+# the in-tree build; KVQ_LIB names another build of the same library (e.g. to compare two builds)
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
 PLANE_K, PLANE_V, PLANE_K_SCALE, PLANE_K_BIAS, PLANE_V_SCALE, PLANE_V_BIAS = range(6)
 PLANES = ("k", "v", "k_scale", "k_bias", "v_scale", "v_bias")
@@ -59,6 +61,7 @@ class DecodeShape(ctypes.Structure):
 
 
 ENGINE_AUTO, ENGINE_VECTOR, ENGINE_MATRIX = 0, 1, 2
+TIMING_PREP, TIMING_PARTIAL, TIMING_MERGE = 0, 1, 2
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -99,6 +102,9 @@ def lib() -> ctypes.CDLL:
                                                          ctypes.POINTER(DecodeShape), _P, ctypes.c_size_t, _P]),
             "kv_gather_debug": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                _P * 6, _P]),
+            "kvq_timing_enable": (ctypes.c_int, [ctypes.c_int32]),
+            "kvq_timing_read": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
+                                               ctypes.POINTER(ctypes.c_int32)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -132,6 +138,19 @@ def _need_cuda(*tensors):
 
 
 # ------------------------------------------------------------------ C ABI, same names
+
+def kvq_timing_enable(on: bool) -> None:
+    """Start (True) or stop (False) bracketing the library's kernel launches with events."""
+    _check(lib().kvq_timing_enable(1 if on else 0))
+
+
+def kvq_timing_read(kind: int):
+    """(mean ms, count) of the launches of `kind` (TIMING_PREP / _PARTIAL / _MERGE) recorded since
+    the last read; waits for their events."""
+    avg, n = ctypes.c_double(0.0), ctypes.c_int32(0)
+    _check(lib().kvq_timing_read(kind, ctypes.byref(avg), ctypes.byref(n)))
+    return float(avg.value), int(n.value)
+
 
 def kv_pool_plane_bytes(desc: PoolDesc, plane: int) -> int:
     return int(lib().kv_pool_plane_bytes(ctypes.byref(desc), plane))

@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "kernels.hpp"
 
@@ -212,9 +213,84 @@ WsLayout workspace_layout(const kvq_pool* pool, const kvq_decode_shape* s, int p
   return L;
 }
 
+// Launch timing: event pairs around the launches of each kind, kept until read.
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;                 // created events, reused
+  size_t next = 0;                              // first unused event of the pool
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[3];
+};
+Timing g_timing;
+
+hipEvent_t timing_event() {                     // under g_timing.mu
+  if (g_timing.next == g_timing.pool.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_timing.pool.push_back(e);
+  }
+  return g_timing.pool[g_timing.next++];
+}
+
+void timing_forget() {                          // under g_timing.mu
+  for (auto& r : g_timing.rec) r.clear();
+  g_timing.next = 0;
+}
+
+// runs launch() (returns hipError_t), bracketed by two events on st when timing is on
+template <class F>
+hipError_t timed(int kind, hipStream_t st, F launch) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  {
+    std::lock_guard<std::mutex> g(g_timing.mu);
+    if (g_timing.on) {
+      e0 = timing_event();
+      e1 = timing_event();
+    }
+  }
+  if (e0 && e1) (void)hipEventRecord(e0, st);
+  const hipError_t r = launch();
+  if (e0 && e1) {
+    (void)hipEventRecord(e1, st);
+    std::lock_guard<std::mutex> g(g_timing.mu);
+    g_timing.rec[kind].push_back({e0, e1});
+  }
+  return r;
+}
+
 }  // namespace
 
 extern "C" {
+
+int kvq_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> g(g_timing.mu);
+  g_timing.on = on != 0;
+  timing_forget();
+  return KVQ_OK;
+}
+
+int kvq_timing_read(int32_t kind, double* avg_ms, int32_t* count) {
+  if (kind < KVQ_TIMING_PREP || kind > KVQ_TIMING_MERGE || !avg_ms || !count)
+    return fail(KVQ_ERR_INVALID, "kvq_timing_read: bad kind or NULL output");
+  std::lock_guard<std::mutex> g(g_timing.mu);
+  double sum = 0.0;
+  int n = 0;
+  for (auto& pr : g_timing.rec[kind]) {
+    hipError_t e = hipEventSynchronize(pr.second);
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) return hip_fail(e, "kvq_timing_read");
+    sum += ms;
+    ++n;
+  }
+  g_timing.rec[kind].clear();
+  bool any = false;
+  for (auto& r : g_timing.rec) any |= !r.empty();
+  if (!any) g_timing.next = 0;                  // every event is free again
+  *avg_ms = n ? sum / n : 0.0;
+  *count = n;
+  return KVQ_OK;
+}
 
 const char* kvq_last_error(void) { return g_err.c_str(); }
 
@@ -339,9 +415,15 @@ struct Plan {
 };
 
 hipError_t launch_plan_partial(const Plan& P, const kvq_pool* pool, int B, hipStream_t st, bool q_ready = false) {
-  if (P.mfma) return kvq::launch_partial_mfma(P.a, pool->desc.head_dim, st);
-  return kvq::launch_partial(P.a, pool->desc.bits, pool->desc.head_dim, pool->desc.group_size, P.qvw, B, q_ready,
-                             st);
+  return timed(KVQ_TIMING_PARTIAL, st, [&] {
+    if (P.mfma) return kvq::launch_partial_mfma(P.a, pool->desc.head_dim, st);
+    return kvq::launch_partial(P.a, pool->desc.bits, pool->desc.head_dim, pool->desc.group_size, P.qvw, B, q_ready,
+                               st);
+  });
+}
+
+hipError_t launch_plan_merge(const Plan& P, int B, hipStream_t st) {
+  return timed(KVQ_TIMING_MERGE, st, [&] { return kvq::launch_merge(P.m, B, st); });
 }
 
 int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, const int32_t* lengths, float scale,
@@ -416,7 +498,7 @@ int paged_decode_merge(const kvq_pool* pool, const int32_t* lengths, const kvq_d
   if (int r = plan(nullptr, pool, nullptr, lengths, 0.0f, shape, const_cast<void*>(workspace), workspace_bytes, out,
                    false, true, &P))
     return r;
-  hipError_t e = kvq::launch_merge(P.m, shape->batch, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_plan_merge(P, shape->batch, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return KVQ_OK;
 }
@@ -430,7 +512,7 @@ int paged_decode_attention(const uint16_t* q, const kvq_pool* pool, const int32_
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_plan_partial(P, pool, shape->batch, st);
   if (e != hipSuccess) return hip_fail(e, "partial launch");
-  e = kvq::launch_merge(P.m, shape->batch, st);
+  e = launch_plan_merge(P, shape->batch, st);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return KVQ_OK;
 }
@@ -457,7 +539,9 @@ int step_partial(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new
   ap.group = d.group_size;
   ap.num_slots = (int64_t)d.num_blocks * d.block_size;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = kvq::launch_step_prep(ap, P.a, d.bits, d.head_dim, d.group_size, P.qvw, !P.mfma, shape->batch, st);
+  hipError_t e = timed(KVQ_TIMING_PREP, st, [&] {
+    return kvq::launch_step_prep(ap, P.a, d.bits, d.head_dim, d.group_size, P.qvw, !P.mfma, shape->batch, st);
+  });
   if (e != hipSuccess) return hip_fail(e, "step launch");
   e = launch_plan_partial(P, pool, shape->batch, st, true);
   if (e != hipSuccess) return hip_fail(e, "partial launch");
@@ -474,7 +558,7 @@ int paged_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* 
   if (int r = step_partial(q, k_new, v_new, pool, block_table, lengths, scale, shape, workspace, workspace_bytes,
                            out, true, stream, &P))
     return r;
-  hipError_t e = kvq::launch_merge(P.m, shape->batch, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_plan_merge(P, shape->batch, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return KVQ_OK;
 }

@@ -216,6 +216,21 @@ int kv_gather_debug(const kvq_pool* pool, const int32_t* block_table, const int3
                     int32_t batch, int32_t max_blocks_per_seq, int32_t max_len,
                     void* const out_planes[KVQ_NUM_PLANES], void* stream);
 
+/* Launch timing, a measurement aid.  While on, every launch of the kinds below records one
+ * hipEvent on its stream right before it and one right after it, so an event pair brackets the
+ * kernel alone (events on the kernel's own stream, not the caller's view of it):
+ *   KVQ_TIMING_PREP    the decode step's first kernel (append of the new rows + q copy)
+ *   KVQ_TIMING_PARTIAL the partial kernel (outside the decode step it also brackets the q copy
+ *                      the vector engine launches right before it)
+ *   KVQ_TIMING_MERGE   the merge kernel
+ * kvq_timing_enable(1) starts recording, (0) stops it; both forget what was recorded.
+ * kvq_timing_read(kind, &avg_ms, &count) waits for the kind's recorded events, returns the mean
+ * duration of its launches since the last read (0 and count 0 if none) and forgets them.
+ * Process-wide state behind a lock; the events are the library's, created on first use. */
+typedef enum kvq_timing_kind { KVQ_TIMING_PREP = 0, KVQ_TIMING_PARTIAL = 1, KVQ_TIMING_MERGE = 2 } kvq_timing_kind;
+int kvq_timing_enable(int32_t on);
+int kvq_timing_read(int32_t kind, double* avg_ms, int32_t* count);
+
 /* Message for the calling thread's last failing call ("" if none). */
 const char* kvq_last_error(void);
 

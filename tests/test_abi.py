@@ -43,6 +43,16 @@ def test_every_declared_symbol_is_exported(lib):
         assert getattr(lib, name) is not None
 
 
+def test_timing_without_launches(lib):
+    """Launch timing: nothing recorded reads as (0 ms, 0 launches); a bad kind is rejected."""
+    kvq.kvq_timing_enable(True)
+    for kind in (kvq.TIMING_PREP, kvq.TIMING_PARTIAL, kvq.TIMING_MERGE):
+        assert kvq.kvq_timing_read(kind) == (0.0, 0)
+    kvq.kvq_timing_enable(False)
+    with pytest.raises(kvq.KvqError, match="KVQ_ERR_INVALID"):
+        kvq.kvq_timing_read(7)
+
+
 def test_struct_layouts():
     assert ctypes.sizeof(kvq.PoolDesc) == 24
     assert ctypes.sizeof(kvq.DecodeShape) == 32
