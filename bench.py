@@ -150,19 +150,21 @@ def main():
     torch.cuda.set_device(dev)
 
     if args.probe_read:
-        # achievable streaming-read rate: a sum over BYTES of f32 (reads BYTES, writes one value)
-        src = torch.ones(args.probe_read // 4, dtype=torch.float32, device=dev)
+        # achievable streaming-read rate: row sums over BYTES of f32 in rows of 32 KiB (reads BYTES,
+        # writes 1/8192 of it)
+        src = torch.ones(args.probe_read // 4 // 8192, 8192, dtype=torch.float32, device=dev)
         for _ in range(3):
-            acc = src.sum()
+            acc = src.sum(dim=1)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
         for _ in range(args.steps):
-            acc = src.sum()
+            acc = src.sum(dim=1)
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
-        print(json.dumps({"probe": "read (torch.sum)", "bytes_read": src.numel() * 4,
+        del acc
+        print(json.dumps({"probe": "read (torch row sums)", "bytes_read": src.numel() * 4,
                           "us_per_read": round(ms * 1e3, 2),
                           "GB_per_s": round(src.numel() * 4 / (ms * 1e-3) / 1e9, 1)}))
         return

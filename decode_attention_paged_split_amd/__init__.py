@@ -28,7 +28,7 @@ __all__ = [
     "kv_pool_destroy", "kv_pool_plane_bytes", "kv_append_quantize", "paged_decode_workspace_bytes",
     "paged_decode_partition_tokens", "paged_decode_attention", "paged_decode_partial",
     "paged_decode_merge", "paged_decode_step", "paged_decode_step_partial", "kv_gather_debug", "make_shape", "gather", "decode_step",
-    "kvq_timing_enable", "kvq_timing_read", "TIMING_PREP", "TIMING_PARTIAL", "TIMING_MERGE",
+    "kvq_timing_enable", "kvq_timing_read", "TIMING_PREP", "TIMING_PARTIAL", "TIMING_MERGE", "PARTITION_AUTO", "PARTITION_STREAM",
     "PLANES", "LIB_PATH",
 ]
 
@@ -62,6 +62,7 @@ class DecodeShape(ctypes.Structure):
 
 ENGINE_AUTO, ENGINE_VECTOR, ENGINE_MATRIX = 0, 1, 2
 TIMING_PREP, TIMING_PARTIAL, TIMING_MERGE = 0, 1, 2
+PARTITION_AUTO, PARTITION_STREAM = 0, -1
 
 
 _lib: Optional[ctypes.CDLL] = None

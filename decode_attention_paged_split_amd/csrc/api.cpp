@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -98,17 +99,28 @@ int qvw_for(int qv, int bits, int D, int gs) {
 // Tokens per split-K partition for the fixed-partition schedule; 0 selects the balanced
 // stream schedule (every wave gets an equal share of all cached tokens).  KVQ_PARTITION_TOKENS
 // (> 0) overrides an automatic choice, for sweeps.
+bool use_mfma(const kvq_decode_shape* s) { return s->engine == KVQ_ENGINE_MATRIX; }
+int qgroups_of(const kvq_pool* pool, const kvq_decode_shape* s);
+
 int choose_partition(const kvq_pool* pool, const kvq_decode_shape* s) {
-  (void)pool;
   if (s->partition_tokens > 0) return s->partition_tokens;
+  if (s->partition_tokens == KVQ_PARTITION_STREAM) return 0;
   if (const char* e = std::getenv("KVQ_PARTITION_TOKENS")) {
     const int v = std::atoi(e);
     if (v > 0) return v;
   }
-  return 0;
+  if (use_mfma(s)) return 0;
+  // A stream too short to give every compute unit a full range of 8 tiles (at most
+  // B * max_len * HK * query groups tokens: the lengths themselves are on the device) runs as
+  // fixed partitions instead, sized so that there are about as many partitions as compute
+  // units: then every tile has a compute unit of its own and each output row has few partials
+  // to merge, where the stream would pile a range's tiles on one unit.
+  const double bound = (double)s->batch * s->max_len * pool->desc.num_kv_heads * qgroups_of(pool, s);
+  const double full = (double)device_cus() * kvq::VALU_STREAM_WAVES * kvq::VALU_TILE;
+  if (bound >= full) return 0;
+  const double per = bound / device_cus();
+  return kvq::VALU_TILE * std::max(1, (int)std::ceil(per / kvq::VALU_TILE));
 }
-
-bool use_mfma(const kvq_decode_shape* s) { return s->engine == KVQ_ENGINE_MATRIX; }
 
 // Stream schedule: the most ranges the stream is cut into and the partial slots per (unit, range).
 // Every range's waves are resident at once.  The vector engine launches one workgroup of 8 waves
@@ -159,7 +171,8 @@ int validate_shape(const kvq_pool* pool, const kvq_decode_shape* s) {
   if ((long)s->max_blocks_per_seq * pool->desc.block_size < s->max_len)
     return fail(KVQ_ERR_RANGE, "max_len %d exceeds the block table's capacity %ld tokens", s->max_len,
                 (long)s->max_blocks_per_seq * pool->desc.block_size);
-  if (s->partition_tokens < 0) return fail(KVQ_ERR_INVALID, "partition_tokens must be >= 0");
+  if (s->partition_tokens < KVQ_PARTITION_STREAM)
+    return fail(KVQ_ERR_INVALID, "partition_tokens must be > 0, 0 (automatic) or -1 (balanced stream)");
   const int pt = choose_partition(pool, s);
   if (pt > 0 && (s->max_len + pt - 1) / pt > MAX_PARTS)
     return fail(KVQ_ERR_UNSUPPORTED, "more than %d partitions (max_len %d, partition %d)", MAX_PARTS,
@@ -175,7 +188,7 @@ int validate_shape(const kvq_pool* pool, const kvq_decode_shape* s) {
                                        "group_size 64");
     if (pt > 0)
       return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core engine runs the balanced stream schedule only "
-                                       "(partition_tokens = 0)");
+                                       "(partition_tokens 0 or -1)");
   } else if (!kvq::partial_supported(pool->desc.bits, pool->desc.head_dim, pool->desc.group_size,
                                      qvw_for(qv, pool->desc.bits, pool->desc.head_dim, pool->desc.group_size))) {
     return fail(KVQ_ERR_UNSUPPORTED, "no kernel for bits=%d D=%d", pool->desc.bits, pool->desc.head_dim);

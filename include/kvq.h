@@ -121,13 +121,19 @@ int kv_append_quantize(kvq_pool* pool, const uint16_t* k, const uint16_t* v,
  * groups put all of a KV head's rows on the matrix cores. */
 #define KVQ_MAX_Q_ROWS 128
 
+enum { KVQ_PARTITION_AUTO = 0, KVQ_PARTITION_STREAM = -1 };
+
 typedef struct kvq_decode_shape {
   int32_t batch;               /* B sequences */
   int32_t num_q_heads;         /* HQ, a multiple of the pool's HK */
   int32_t q_rows;              /* N query rows per sequence, 1..KVQ_MAX_Q_ROWS */
   int32_t max_blocks_per_seq;  /* columns of block_table */
   int32_t max_len;             /* host upper bound on every lengths[b] (sizes the grid) */
-  int32_t partition_tokens;    /* tokens per split-K partition; 0 = automatic */
+  int32_t partition_tokens;    /* > 0: fixed split-K partitions of this many tokens;
+                                  KVQ_PARTITION_AUTO (0): the balanced stream, or, when B * max_len *
+                                  HK * query groups is too few tokens to give every compute unit
+                                  8 tiles of 64, fixed partitions of about one per compute unit;
+                                  KVQ_PARTITION_STREAM (-1): the balanced stream */
   int32_t out_f32;             /* 0: out is bf16; 1: out is f32 (unrounded merge result) */
   int32_t engine;              /* kvq_engine: which units compute q.k and P.V */
 } kvq_decode_shape;
@@ -137,7 +143,7 @@ typedef struct kvq_decode_shape {
  *   KVQ_ENGINE_VECTOR: vector ALU -- v_dot2_f32_bf16 for q.k, f32 FMA for P.V; every format.
  *   KVQ_ENGINE_MATRIX: matrix cores -- q.k with exact bf16 products, P.V with exact f16 codes
  *     against the weight split into two f16 halves (~2^-22 relative); 4-bit pages, head_dim
- *     128 or 256, partition_tokens == 0 only.  It serves the GQA groups where the vector ALU
+ *     128 or 256, the balanced stream only (partition_tokens <= 0).  It serves the GQA groups where the vector ALU
  *     rather than HBM bounds the pass ([P50] multi-query.ts puts a KV head's query rows on the
  *     matrix unit for the same reason).
  *   KVQ_ENGINE_AUTO: the vector engine. */
@@ -147,7 +153,8 @@ enum kvq_engine { KVQ_ENGINE_AUTO = 0, KVQ_ENGINE_VECTOR = 1, KVQ_ENGINE_MATRIX 
  * invalid).  The workspace holds per-partition partial outputs (f32). */
 size_t paged_decode_workspace_bytes(const kvq_pool* pool, const kvq_decode_shape* shape);
 
-/* Partition size the library picks for partition_tokens == 0 (for reporting). */
+/* Partition size the library uses for this shape: the fixed partition's tokens, or 0 for the
+ * balanced stream (for reporting). */
 int32_t paged_decode_partition_tokens(const kvq_pool* pool, const kvq_decode_shape* shape);
 
 /* Decode attention for N <= KVQ_MAX_Q_ROWS query rows per sequence read straight from the pages

@@ -131,7 +131,7 @@ class _FakePool:
 @pytest.mark.parametrize("mut,code", [(dict(q_rows=129), -2), (dict(q_rows=0), -2), (dict(num_q_heads=5), -2),
                                       (dict(batch=0), -1), (dict(max_len=0), -1),
                                       (dict(max_blocks_per_seq=1, max_len=1000), -6),
-                                      (dict(partition_tokens=-1), -1), (dict(engine=3), -1),
+                                      (dict(partition_tokens=-2), -1), (dict(engine=3), -1),
                                       (dict(engine=2, partition_tokens=64), -2)])
 def test_decode_shape_rejected(lib, mut, code):
     p = _FakePool()
@@ -206,6 +206,22 @@ def test_automatic_schedule_is_the_balanced_stream(lib, monkeypatch):
     assert need == _ws_bytes(slots, 256, qvecs=32 * 16)   # 8 waves per range, 8 vectors
     s.partition_tokens = 300
     assert lib.paged_decode_partition_tokens(p.handle, ctypes.byref(s)) == 300
+    s.partition_tokens = kvq.PARTITION_STREAM
+    assert lib.paged_decode_partition_tokens(p.handle, ctypes.byref(s)) == 0
+    p.close()
+
+
+@pytest.mark.parametrize("batch,max_len,expect", [(1, 2048, 64), (3, 16384, 384), (4, 16384, 0), (32, 32197, 0)])
+def test_automatic_schedule_for_short_streams(lib, monkeypatch, batch, max_len, expect):
+    """Automatic choice: fixed partitions of about one per compute unit (a multiple of 64 tokens)
+    while B * max_len * HK * query groups is below 256 compute units x 8 tiles of 64 tokens, the
+    balanced stream from there on; the matrix engine always runs the stream."""
+    monkeypatch.delenv("KVQ_PARTITION_TOKENS", raising=False)
+    p = _FakePool()
+    s = kvq.DecodeShape(batch, 16, 1, 1100, max_len, kvq.PARTITION_AUTO, 0, 0)
+    assert lib.paged_decode_partition_tokens(p.handle, ctypes.byref(s)) == expect
+    s.engine = kvq.ENGINE_MATRIX
+    assert lib.paged_decode_partition_tokens(p.handle, ctypes.byref(s)) == 0
     p.close()
 
 

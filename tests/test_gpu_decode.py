@@ -50,7 +50,7 @@ def filled():
 
 
 @pytest.mark.parametrize("name", list(SMALL))
-@pytest.mark.parametrize("pt", [0, 64, 333])
+@pytest.mark.parametrize("pt", [kvq.PARTITION_STREAM, kvq.PARTITION_AUTO, 64, 333])
 def test_decode_parity(filled, name, pt):
     print(f"decode {name} pt={pt}", flush=True)
     w, pool, ref = filled(name, **SMALL[name])
@@ -81,8 +81,8 @@ def test_deterministic(filled):
     a = G.run_decode(w, pool, partition_tokens=64)
     b = G.run_decode(w, pool, partition_tokens=64)
     assert np.array_equal(a, b)
-    a = G.run_decode(w, pool)
-    b = G.run_decode(w, pool)
+    a = G.run_decode(w, pool, partition_tokens=kvq.PARTITION_STREAM)
+    b = G.run_decode(w, pool, partition_tokens=kvq.PARTITION_STREAM)
     assert np.abs(a - b).max() <= 1e-6 * np.abs(a).max()
 
 
@@ -103,7 +103,7 @@ def test_decode_edge_cases(filled, case):
     name = case.pop("name")
     print(f"edge {name} {case}", flush=True)
     w, pool, ref = filled(name, **case)
-    for pt in (0, 7):
+    for pt in (kvq.PARTITION_STREAM, kvq.PARTITION_AUTO, 7):
         got = G.run_decode(w, pool, partition_tokens=pt)
         G.check_f32(got, ref, tag=f"{name} {case} pt={pt}")
 
@@ -152,7 +152,7 @@ def test_precondition_violations_do_not_fault_or_leak(filled):
     lengths = w.lengths.astype(np.int32).copy()
     lengths[1] = 0
     lengths[2] = w.max_len + 500
-    for pt in (0, 64):
+    for pt in (kvq.PARTITION_STREAM, 64):
         got = G.run_decode(w, pool, partition_tokens=pt, lengths=G.i32_dev(lengths))
         keep = [0] + list(range(3, w.B))
         G.check_f32(got[keep], ref[keep], tag=f"pt={pt}")

@@ -39,7 +39,7 @@ def test_decode_groups(bits, D, group):
     ref = attention.workload_output(w)
     pool = G.new_pool(w)
     G.fill_pool(w, pool)
-    for pt in (0, 96):
+    for pt in (kvq.PARTITION_STREAM, 96):
         got = G.run_decode(w, pool, partition_tokens=pt)
         G.check_f32(got, ref, tag=f"bits={bits} D={D} group={group} pt={pt}")
     pool.close()

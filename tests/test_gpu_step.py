@@ -46,7 +46,7 @@ def _new_rows(w):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("pt", [0, 64])
+@pytest.mark.parametrize("pt", [kvq.PARTITION_STREAM, kvq.PARTITION_AUTO, 64])
 def test_step_matches_two_call_path_and_oracle(name, pt):
     print(f"step {name} pt={pt}", flush=True)
     w = make_workload(name, **CASES[name])
