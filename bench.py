@@ -150,23 +150,22 @@ def main():
     torch.cuda.set_device(dev)
 
     if args.probe_read:
-        # achievable streaming-read rate: row sums over BYTES of f32 in rows of 32 KiB (reads BYTES,
-        # writes 1/8192 of it)
-        src = torch.ones(args.probe_read // 4 // 8192, 8192, dtype=torch.float32, device=dev)
+        # achievable streaming-read rate: the library's read probe over BYTES (every byte read once)
+        buf = torch.ones(args.probe_read // 4, dtype=torch.float32, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
         for _ in range(3):
-            acc = src.sum(dim=1)
+            kvq.kvq_probe_read(buf, sink)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
         for _ in range(args.steps):
-            acc = src.sum(dim=1)
+            kvq.kvq_probe_read(buf, sink)
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
-        del acc
-        print(json.dumps({"probe": "read (torch row sums)", "bytes_read": src.numel() * 4,
+        print(json.dumps({"probe": "read (kvq_probe_read)", "bytes_read": buf.numel() * 4,
                           "us_per_read": round(ms * 1e3, 2),
-                          "GB_per_s": round(src.numel() * 4 / (ms * 1e-3) / 1e9, 1)}))
+                          "GB_per_s": round(buf.numel() * 4 / (ms * 1e-3) / 1e9, 1)}))
         return
 
     if args.probe_copy:

@@ -28,7 +28,7 @@ __all__ = [
     "kv_pool_destroy", "kv_pool_plane_bytes", "kv_append_quantize", "paged_decode_workspace_bytes",
     "paged_decode_partition_tokens", "paged_decode_attention", "paged_decode_partial",
     "paged_decode_merge", "paged_decode_step", "paged_decode_step_partial", "kv_gather_debug", "make_shape", "gather", "decode_step",
-    "kvq_timing_enable", "kvq_timing_read", "TIMING_PREP", "TIMING_PARTIAL", "TIMING_MERGE", "PARTITION_AUTO", "PARTITION_STREAM",
+    "kvq_timing_enable", "kvq_timing_read", "kvq_probe_read", "TIMING_PREP", "TIMING_PARTIAL", "TIMING_MERGE", "PARTITION_AUTO", "PARTITION_STREAM",
     "PLANES", "LIB_PATH",
 ]
 
@@ -103,6 +103,7 @@ def lib() -> ctypes.CDLL:
                                                          ctypes.POINTER(DecodeShape), _P, ctypes.c_size_t, _P]),
             "kv_gather_debug": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                _P * 6, _P]),
+            "kvq_probe_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
             "kvq_timing_enable": (ctypes.c_int, [ctypes.c_int32]),
             "kvq_timing_read": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
                                                ctypes.POINTER(ctypes.c_int32)]),
@@ -143,6 +144,12 @@ def _need_cuda(*tensors):
 def kvq_timing_enable(on: bool) -> None:
     """Start (True) or stop (False) bracketing the library's kernel launches with events."""
     _check(lib().kvq_timing_enable(1 if on else 0))
+
+
+def kvq_probe_read(buf, sink, stream=None) -> None:
+    """Enqueue the streaming-read probe over the device tensor buf (sink: a device int32 tensor)."""
+    _need_cuda(buf, sink)
+    _check(lib().kvq_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 
 def kvq_timing_read(kind: int):

@@ -305,6 +305,15 @@ int kvq_timing_read(int32_t kind, double* avg_ms, int32_t* count) {
   return KVQ_OK;
 }
 
+int kvq_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4))
+    return fail(KVQ_ERR_INVALID, "kvq_probe_read: buf (16-byte aligned) and sink must be device pointers");
+  if (bytes == 0 || bytes % 16 != 0) return fail(KVQ_ERR_INVALID, "kvq_probe_read: bytes must be a positive multiple of 16");
+  hipError_t e = kvq::launch_probe_read(buf, bytes, sink, 32 * device_cus(), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return KVQ_OK;
+}
+
 const char* kvq_last_error(void) { return g_err.c_str(); }
 
 const char* kvq_version(void) { return "kvq 0.1 (gfx950)"; }

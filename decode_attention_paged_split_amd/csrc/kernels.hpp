@@ -74,6 +74,8 @@ struct MergeArgs {
 constexpr int Q_BLOCK_WORDS = 20;
 
 hipError_t launch_append(const AppendArgs& a, int bits, hipStream_t stream);
+// streaming-read probe over bytes (a multiple of 16) of buf with `blocks` workgroups of 256
+hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 
 // qvw: query vectors per workgroup (REP * N split into qgroups groups of qvw)

@@ -474,13 +474,18 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
       if (h + 1 < NP) kpart = knext;
     }
 
-    // ---- stage V part 0 of this tile, then start the next tile's loads
-    // (after the last tile these reload the current rows: valid addresses, never used)
+    // ---- stage V part 0 of this tile, then start the next tile's loads.  After a wave's last
+    // tile of a unit there is no next tile: the loads are skipped (a uniform branch), except in
+    // the 4-bit, head-dim-256, 8-vector instance, whose live registers the branch pushes past 256
+    // (spills, 7 % slower); it reloads the current rows instead (valid addresses, never used).
     stage_v(vcur);
     const int row_next = has_next ? row_of(t_next, tbl_next) : row;
-    kcur = load_row_part<KCP>(kplane, row_next, ROWB, 0);
-    load_scales(row_next, scn);
-    vcur = load_row_part<KCP>(vplane, row_next, ROWB, 0);
+    constexpr bool RELOAD = BITS == 4 && D == 256 && QVW == 8;
+    if (RELOAD || has_next) {
+      kcur = load_row_part<KCP>(kplane, row_next, ROWB, 0);
+      load_scales(row_next, scn);
+      vcur = load_row_part<KCP>(vplane, row_next, ROWB, 0);
+    }
 
     // ---- softmax, one token per lane
     const int tok = tt + lane;

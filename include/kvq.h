@@ -238,6 +238,15 @@ typedef enum kvq_timing_kind { KVQ_TIMING_PREP = 0, KVQ_TIMING_PARTIAL = 1, KVQ_
 int kvq_timing_enable(int32_t on);
 int kvq_timing_read(int32_t kind, double* avg_ms, int32_t* count);
 
+/* Streaming-read probe, a measurement aid: enqueues one kernel that reads every byte of buf
+ * (device, 16-byte aligned, bytes a positive multiple of 16) once with 16-byte loads, from 32
+ * workgroups of 256 threads per compute unit, four loads in flight per thread.  It writes
+ * nothing but, in the unlikely case that the folded words hit one fixed constant, sink (a device
+ * uint32 whose content is then undefined); the fold keeps the loads alive.  The caller times it
+ * (events around the call).  Errors: KVQ_ERR_INVALID for NULL or misaligned pointers or a bad
+ * size. */
+int kvq_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Message for the calling thread's last failing call ("" if none). */
 const char* kvq_last_error(void);
 

@@ -53,6 +53,12 @@ def test_timing_without_launches(lib):
         kvq.kvq_timing_read(7)
 
 
+def test_probe_read_rejects_bad_arguments(lib):
+    assert lib.kvq_probe_read(None, 1024, None, None) == -1
+    assert lib.kvq_probe_read(ctypes.c_void_p(256), 1000, ctypes.c_void_p(512), None) == -1   # not x16
+    assert lib.kvq_probe_read(ctypes.c_void_p(255), 1024, ctypes.c_void_p(512), None) == -1   # misaligned
+
+
 def test_struct_layouts():
     assert ctypes.sizeof(kvq.PoolDesc) == 24
     assert ctypes.sizeof(kvq.DecodeShape) == 32
