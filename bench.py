@@ -244,14 +244,27 @@ def main():
     log(f"[bench] warmup {args.warmup} steps done")
 
     def timed(nsteps, flush_buf, shp=shape, wsp=ws):
-        """nsteps timed steps, then as many again under the library's launch timing.  Torch events
-        per step: after the partial pass and after the merge (warm: the previous step's end, or
-        the start event, opens the next step; cold: an event after the 1 GiB write).  The launch
-        timing brackets each kernel with events on its own stream; those event records add a few
-        microseconds between kernels, so the step time comes from the first pass and only the
-        kernel durations from the second.  Returns a dict: ms per step, partial-pass and merge ms
-        lists, wall s, and the mean ms of the prep, partial and merge kernels."""
+        """Warm: nsteps back-to-back steps between two events give the step time; then nsteps
+        with an event after the partial pass and after each merge split it (the previous step's
+        end opens the next step); then nsteps under the library's launch timing, which brackets
+        each kernel with events on its own stream, give the kernels' durations.  Event records
+        between kernels delay the next launch by a few microseconds, so each pass gives only its
+        own figure.  Cold: the 1 GiB write, an event, the step, an event, per step.  Returns a
+        dict: ms per step, partial-pass and merge ms lists, wall s (second pass), and the mean ms
+        of the prep, partial and merge kernels."""
         E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        ms_plain = None
+        if flush_buf is None:
+            # the step time itself: back-to-back steps between two events (an event recorded
+            # between kernels delays the next launch by a few microseconds)
+            a0, a1 = E(), E()
+            torch.cuda.synchronize()
+            a0.record()
+            for i in range(nsteps):
+                step(None, shp, wsp)
+            a1.record()
+            torch.cuda.synchronize()
+            ms_plain = a0.elapsed_time(a1) / nsteps
         ev0 = E()
         mids = [E() for _ in range(nsteps)]
         ends = [E() for _ in range(nsteps)]
@@ -280,8 +293,9 @@ def main():
         par = [o.elapsed_time(m) for o, m in zip(opens, mids)]
         mer = [m.elapsed_time(e) for m, e in zip(mids, ends)]
         tot = [o.elapsed_time(e) for o, e in zip(opens, ends)]
-        ms = float(np.mean(tot)) if flush_buf is not None else ev0.elapsed_time(ends[-1]) / nsteps
-        return {"ms": ms, "par": par, "mer": mer, "wall": wall, "kern": kern}
+        ms = float(np.mean(tot)) if flush_buf is not None else ms_plain
+        return {"ms": ms, "par": par, "mer": mer, "wall": wall, "kern": kern,
+                "ms_with_events": ev0.elapsed_time(ends[-1]) / nsteps}
 
     t = timed(args.steps, flush)
     ms_step, par, mer, wall = t["ms"], t["par"], t["mer"], t["wall"]
