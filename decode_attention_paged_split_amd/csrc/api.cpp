@@ -146,7 +146,9 @@ StreamGeom stream_geom(const kvq_pool* pool, const kvq_decode_shape* s) {
 // query vectors per workgroup (vector ALU) or per wave (matrix cores, padded to 16)
 int qvw_of(const kvq_pool* pool, const kvq_decode_shape* s) {
   const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
-  return use_mfma(s) ? kvq::MFMA_QVW : qvw_for(qv, pool->desc.bits, pool->desc.head_dim, pool->desc.group_size);
+  if (use_mfma(s))
+    return (pool->desc.head_dim == 256 && qv <= kvq::MFMA_PAIR_QVW) ? kvq::MFMA_PAIR_QVW : kvq::MFMA_QVW;
+  return qvw_for(qv, pool->desc.bits, pool->desc.head_dim, pool->desc.group_size);
 }
 
 int qgroups_of(const kvq_pool* pool, const kvq_decode_shape* s) {

@@ -42,7 +42,8 @@ enum : int {
   DPP_QUAD_1032 = 0xB1,      // quad_perm [1,0,3,2]  (lane ^ 1)
   DPP_QUAD_2301 = 0x4E,      // quad_perm [2,3,0,1]  (lane ^ 2)
   DPP_ROW_MIRROR = 0x140,    // lane i <- 15 - i within a row of 16
-  DPP_ROW_HALF_MIRROR = 0x141 // lane i <- 7 - i within each half row of 8
+  DPP_ROW_HALF_MIRROR = 0x141, // lane i <- 7 - i within each half row of 8
+  DPP_ROW_ROR8 = 0x128       // row_ror:8: lane i <- lane (i + 8) % 16 within a row (lane ^ 8)
 };
 
 template <int CTRL>
@@ -76,6 +77,15 @@ __device__ __forceinline__ float xstep(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return OP::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
   }
+}
+
+// All-reduce over the 8 lanes i, i ^ 8, i ^ 16, ..., i ^ 56 (every lane's value may differ):
+// exact xor steps at distances 8, 16 and 32.
+template <class OP>
+__device__ __forceinline__ float xor8_reduce(float x) {
+  x = OP::f(x, dpp<DPP_ROW_ROR8>(x));
+  x = xstep<OP, 16>(x);
+  return xstep<OP, 32>(x);
 }
 
 // All-reduce over aligned blocks of HI lanes, assuming values are uniform over aligned

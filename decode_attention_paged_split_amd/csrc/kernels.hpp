@@ -103,6 +103,9 @@ constexpr bool valu_row_ok(int bits, int D) { return (D * bits / 8) % 16 == 0; }
 bool mfma_supported(int bits, int D, int gs);
 hipError_t launch_partial_mfma(const PartialArgs& a, int D, hipStream_t s);
 constexpr int MFMA_QVW = 16;
+// head dim 256 with at most this many query vectors per KV head: 8 vectors per unit, two token
+// blocks per MFMA (the pair kernel)
+constexpr int MFMA_PAIR_QVW = 8;
 constexpr int MFMA_TILE = 64;
 // vector engine, stream schedule: one workgroup of VALU_STREAM_WAVES waves per compute unit owns
 // a range and shares its 64-token tiles among its waves

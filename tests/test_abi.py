@@ -234,17 +234,21 @@ def test_automatic_schedule_for_short_streams(lib, monkeypatch, batch, max_len, 
 def test_matrix_engine_limits(lib):
     """The matrix-core engine reads 4-bit pages at head dim 128/256 on the stream schedule (4
     ranges per compute unit at head dim 256, a two-wave workgroup each; 8 at 128, a wave each);
-    its workspace holds 16 query vectors per slot."""
+    its workspace holds 16 query vectors per slot, or 8 at head dim 256 when a KV head has at
+    most 8 (the pair kernel)."""
+    for hq in (16, 32):                                   # 8 or 16 query vectors per KV head
+        s = kvq.DecodeShape(32, hq, 1, 1100, 32197, 0, 0, 2)
+        for bits, D, ok in [(4, 256, True), (4, 128, True), (8, 256, False), (16, 128, False), (4, 64, False)]:
+            p = _FakePool(bits=bits, D=D)
+            need = lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s))
+            if ok:
+                qvw = 8 if (D == 256 and hq == 16) else 16
+                slots = ((4 if D == 256 else 8) * 256 + 32 * 2) * qvw
+                assert need == _ws_bytes(slots, D)
+            else:
+                assert need == 0
+            p.close()
     s = kvq.DecodeShape(32, 16, 1, 1100, 32197, 0, 0, 2)
-    for bits, D, ok in [(4, 256, True), (4, 128, True), (8, 256, False), (16, 128, False), (4, 64, False)]:
-        p = _FakePool(bits=bits, D=D)
-        need = lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(s))
-        if ok:
-            slots = ((4 if D == 256 else 8) * 256 + 32 * 2) * 16
-            assert need == _ws_bytes(slots, D)
-        else:
-            assert need == 0
-        p.close()
     d = kvq.PoolDesc(64, 2, 32, 256, 4, 32)
     h = kvq.kv_pool_wrap(d, [256] * 6)
     assert lib.paged_decode_workspace_bytes(h, ctypes.byref(s)) == 0      # matrix engine: group 64 only
