@@ -987,7 +987,6 @@ partial_mfma_pair_kernel(PartialArgs a) {
         if (tt + 2 * MF_TILE < t1) ph_next = trow[tab_idx(tt + 2 * MF_TILE)];
       }
       mf_lds_sync();
-      __builtin_amdgcn_sched_barrier(0);
 
       // ---- q.k for both pairs, then each score's scale and bias: lane (n, g), pair st holds the
       // scores of tokens 16 (2 st + bx) + 4 g + i for vector v
@@ -1006,7 +1005,6 @@ partial_mfma_pair_kernel(PartialArgs a) {
           z[st][i] = fmaf(sb.z, acc1[i], fmaf(sb.w, qsum[1], fmaf(sb.x, acc0[i], sb.y * qsum[0])));
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
 
       // ---- the two halves' scores meet: z = z(dims 0..127) + z(dims 128..255) in both waves
 #pragma unroll
@@ -1060,7 +1058,6 @@ partial_mfma_pair_kernel(PartialArgs a) {
           ls += z[st][i];
         }
       l += ls;
-      __builtin_amdgcn_sched_barrier(0);
 
       // ---- weights w = p * s_v per (pair, token, group), split into f16 hi + lo (each rounded to
       // nearest), both groups of a token packed in one f16 pair and moved by v_perm into the
@@ -1110,8 +1107,7 @@ partial_mfma_pair_kernel(PartialArgs a) {
             o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, blo[st], o[dt], 0, 0, 0);
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+        }
       mf_lds_sync();                              // this wave's LDS is rewritten next tile
     }
 
