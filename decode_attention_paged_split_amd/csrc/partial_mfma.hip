@@ -856,11 +856,16 @@ partial_mfma_split_kernel(PartialArgs a) {
 //    output are added once at the end of a range.
 constexpr int PQ = 8;                             // query vectors per unit
 
+struct PairShared {
+  SpWave w[2];
+  float4 zx[2][2][2][64];                         // partial scores [buffer][wave][pair][lane]
+};
+
 __global__ void __launch_bounds__(128, 2)
 partial_mfma_pair_kernel(PartialArgs a) {
   const KUnpack ku = k_unpack_consts();
   constexpr int D = 256;
-  __shared__ __align__(16) SpShared sh;
+  __shared__ __align__(16) PairShared sh;
 
   const int lane = threadIdx.x & 63;
   const int h = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // dim half of this wave
