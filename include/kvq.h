@@ -11,6 +11,12 @@
  *          src/state/paged/cache.ts
  *   [P47]  "mlx-bun 0.2.0 -> 0.4.0", diff page 47: model/batched-quantized-kv.ts
  *
+ * Environment (tuning sweeps only; unset in normal use):
+ *   KVQ_PARTITION_TOKENS=n  (n > 0) replaces the automatic partition choice of
+ *                           partition_tokens == 0 by fixed partitions of n tokens.
+ *   KVQ_MFMA_RANGES_PER_CU=n  ranges per compute unit of the matrix-core engine's stream
+ *                           (2..16; default 4 at head dim 256, 8 at 128).
+ *
  * Conventions shared by every entry point
  *   - Return value: KVQ_OK (0) or a negative kvq_status.  A failing call enqueues
  *     nothing; kvq_last_error() then returns a message for the calling thread.
