@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3")
+    ap.add_argument("--bits", type=int, default=0, help="page format override: 16 (bf16) or 2..8 (affine)")
+    ap.add_argument("--group", type=int, default=0, help="scale-group override (32, 64 or 128 head dims)")
+    ap.add_argument("--rows", type=int, default=0, help="query rows per sequence override (N)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--engine", choices=["auto", "vector", "matrix"], default="auto",
                     help="partial-pass engine: vector ALU (the default) or matrix cores (4-bit pages)")
@@ -187,10 +190,11 @@ def main():
         return
 
     t_setup = time.time()
-    w = make_workload(args.workload)
+    over = {k: v for k, v in (("bits", args.bits), ("group", args.group), ("N", args.rows)) if v}
+    w = make_workload(args.workload, **over)
     log(f"[bench] workload {w.name}: B={w.B} HQ={w.HQ} HK={w.HK} D={w.D} N={w.N} bits={w.bits} "
         f"BS={w.BS} sum(len)={int(w.lengths.sum())} NB={w.num_blocks}")
-    pool = kvq.Pool(w.num_blocks, w.HK, w.BS, w.D, w.bits, device=dev)
+    pool = kvq.Pool(w.num_blocks, w.HK, w.BS, w.D, w.bits, w.group, device=dev)
     new_k, new_v, new_slots = [], [], []
     # the draws of each sequence are independent (own seed), so a few threads generate them
     # ahead of the device appends (NumPy's generators release the GIL)
@@ -340,7 +344,7 @@ def main():
             "hbm": hbm, "alu": alu, "kernel_source_hash": src_hash}
 
     variants = {}
-    if args.engine == "auto" and w.bits == 4 and w.D in (128, 256) and args.partition_tokens == 0:
+    if args.engine == "auto" and w.bits == 4 and w.group == 64 and w.D in (128, 256) and args.partition_tokens <= 0:
         # the separately flagged matrix-core engine on the same inputs, timed the same way
         shp_m = kvq.make_shape(pool, w.B, w.HQ, w.N, w.max_blocks, w.max_len, 0, False, kvq.ENGINE_MATRIX)
         ws_m = torch.empty(kvq.paged_decode_workspace_bytes(pool, shp_m), dtype=torch.uint8, device=dev)
@@ -362,9 +366,10 @@ def main():
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"{w.name}: 4-bit affine g64 paged KV, B={w.B}, lengths U[4096,32768] "
-                               f"(sum {int(w.lengths.sum())}), BS={w.BS}, HQ={w.HQ}, HK={w.HK}, D={w.D}, "
-                               f"N={w.N}" if w.name == "c3" else w.name,
+        "config": {"workload": (f"{w.name}: 4-bit affine g64 paged KV, B={w.B}, lengths U[4096,32768] "
+                                f"(sum {int(w.lengths.sum())}), BS={w.BS}, HQ={w.HQ}, HK={w.HK}, D={w.D}, "
+                                f"N={w.N}") if (w.name == "c3" and not over) else
+                               (w.name + "".join(f" {k}={v}" for k, v in over.items())),
                    "global_batch": w.B, "seq_len": w.max_len, "parallelism": "single GPU",
                    "partition_tokens": pt, "cold": bool(args.cold), "engine": args.engine},
         "us_per_step": round(ms_step * 1e3, 2), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
