@@ -238,7 +238,10 @@ struct Timing {
 };
 Timing g_timing;
 
+constexpr size_t TIMING_MAX_EVENTS = 65536;     // 32768 launches between two reads
+
 hipEvent_t timing_event() {                     // under g_timing.mu
+  if (g_timing.next >= TIMING_MAX_EVENTS) return nullptr;   // full: later launches go unrecorded
   if (g_timing.next == g_timing.pool.size()) {
     hipEvent_t e = nullptr;
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
@@ -258,7 +261,7 @@ hipError_t timed(int kind, hipStream_t st, F launch) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
   {
     std::lock_guard<std::mutex> g(g_timing.mu);
-    if (g_timing.on) {
+    if (g_timing.on && g_timing.next + 2 <= TIMING_MAX_EVENTS) {
       e0 = timing_event();
       e1 = timing_event();
     }

@@ -239,7 +239,8 @@ int kv_gather_debug(const kvq_pool* pool, const int32_t* block_table, const int3
  * kvq_timing_enable(1) starts recording, (0) stops it; both forget what was recorded.
  * kvq_timing_read(kind, &avg_ms, &count) waits for the kind's recorded events, returns the mean
  * duration of its launches since the last read (0 and count 0 if none) and forgets them.
- * Process-wide state behind a lock; the events are the library's, created on first use. */
+ * Process-wide state behind a lock; the events are the library's, created on first use.  At most
+ * 32768 launches are recorded between reads (later ones run unrecorded). */
 typedef enum kvq_timing_kind { KVQ_TIMING_PREP = 0, KVQ_TIMING_PARTIAL = 1, KVQ_TIMING_MERGE = 2 } kvq_timing_kind;
 int kvq_timing_enable(int32_t on);
 int kvq_timing_read(int32_t kind, double* avg_ms, int32_t* count);
