@@ -33,7 +33,8 @@ def visible(length: int, N: int, i: int) -> int:
 
 
 def attend_one(qv: np.ndarray, K: np.ndarray, V: np.ndarray, T: int, scale: float) -> np.ndarray:
-    """One query vector against the first T rows of K, V ([len, D] f64); two-pass softmax."""
+    """One query vector against the first T rows of K [len, D] and V [len, DV] (f64); two-pass
+    softmax."""
     z = scale * (K[:T] @ qv)
     M = z.max()
     p = np.exp(z - M)
@@ -42,12 +43,14 @@ def attend_one(qv: np.ndarray, K: np.ndarray, V: np.ndarray, T: int, scale: floa
 
 def decode_attention(q: np.ndarray, K: Sequence[np.ndarray], V: Sequence[np.ndarray],
                      lengths: np.ndarray, scale: float) -> np.ndarray:
-    """q [B, HQ, N, D] f64; K[b], V[b] [len_b, HK, D] f64 -> out [B, HQ, N, D] f64.
+    """q [B, HQ, N, D] f64; K[b] [len_b, HK, D], V[b] [len_b, HK, DV] f64 -> out [B, HQ, N, DV] f64
+    (the value head dim may differ from the key's: paged.ts's DK and DV).
 
     One (sequence, KV head) at a time, with its REP * N query vectors as one matrix.
     """
     B, HQ, N, D = q.shape
-    out = np.zeros((B, HQ, N, D), dtype=np.float64)
+    DV = V[0].shape[2] if len(V) else D
+    out = np.zeros((B, HQ, N, DV), dtype=np.float64)
     for b in range(B):
         L = int(lengths[b])
         HK = K[b].shape[1]
@@ -63,7 +66,7 @@ def decode_attention(q: np.ndarray, K: Sequence[np.ndarray], V: Sequence[np.ndar
             M = Z.max(axis=1, keepdims=True)
             P = np.where(mask, np.exp(Z - M), 0.0)
             O = (P @ Vg) / P.sum(axis=1, keepdims=True)
-            out[b, g * REP:(g + 1) * REP] = O.reshape(REP, N, D)
+            out[b, g * REP:(g + 1) * REP] = O.reshape(REP, N, DV)
     return out
 
 
@@ -101,14 +104,15 @@ def q_f64(q_bits: np.ndarray) -> np.ndarray:
 
 
 def workload_kv(w, b: int):
-    """Dequantized K, V of sequence b of a workload (contiguous path), [len, HK, D] f64."""
+    """Dequantized K [len, HK, D] and V [len, HK, DV] of sequence b of a workload (contiguous
+    path), f64."""
     k, v = w.kv(b)
     return rows_dequantized(k, v, w.bits, w.group)
 
 
 def workload_pool(w, seqs=None) -> Pool:
     """A pool filled with the rows of the chosen sequences of a workload (all by default)."""
-    pool = Pool(w.num_blocks, w.HK, w.BS, w.D, w.bits, w.group)
+    pool = Pool(w.num_blocks, w.HK, w.BS, w.D, w.bits, w.group, v_head_dim=w.DV)
     for b in (range(w.B) if seqs is None else seqs):
         k, v = w.kv(b)
         pool.write(k, v, w.slots(b))
@@ -116,7 +120,7 @@ def workload_pool(w, seqs=None) -> Pool:
 
 
 def workload_output(w, seqs=None) -> np.ndarray:
-    """The decode output of a workload (or of some of its sequences), f64 [len(seqs), HQ, N, D]."""
+    """The decode output of a workload (or of some of its sequences), f64 [len(seqs), HQ, N, DV]."""
     seqs = list(range(w.B)) if seqs is None else list(seqs)
     q = q_f64(w.q_bits[seqs])
     K, V = [], []

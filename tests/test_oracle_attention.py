@@ -36,13 +36,14 @@ def _sdpa_ref(q, K, V, lengths, scale):
     return np.stack(outs)
 
 
-def _tiny(bits, B=2, HQ=4, HK=2, D=64, N=1, lens=(37, 64), seed=3):
+def _tiny(bits, B=2, HQ=4, HK=2, D=64, N=1, lens=(37, 64), seed=3, DV=None):
     rng = np.random.default_rng(seed)
+    DV = D if DV is None else DV
     q = bf16.to_f64(bf16.rne(rng.standard_normal((B, HQ, N, D)).astype(np.float32)))
     K, V = [], []
     for b in range(B):
         kb = bf16.rne(rng.standard_normal((lens[b], HK, D)).astype(np.float32))
-        vb = bf16.rne(rng.standard_normal((lens[b], HK, D)).astype(np.float32))
+        vb = bf16.rne(rng.standard_normal((lens[b], HK, DV)).astype(np.float32))
         k, v = paged.rows_dequantized(kb, vb, bits)
         K.append(k), V.append(v)
     return q, K, V, np.array(lens)
@@ -57,6 +58,30 @@ def test_matches_torch_sdpa(bits, D, N):
     got = attention.decode_attention(q, K, V, lens, scale)
     ref = _sdpa_ref(q, K, V, lens, scale)
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("bits", [16, 4, 2])
+@pytest.mark.parametrize("D,DV", [(128, 64), (64, 128), (256, 128), (128, 256)])
+def test_value_head_dim_of_its_own_matches_torch_sdpa(bits, D, DV):
+    """V rows narrower or wider than K's (the pages' DK != DV): torch's SDPA takes a value dim
+    of its own, and the oracle's output has the value rows' width."""
+    q, K, V, lens = _tiny(bits, D=D, DV=DV, N=2, HQ=6, HK=3)
+    scale = 1.0 / math.sqrt(D)
+    got = attention.decode_attention(q, K, V, lens, scale)
+    assert got.shape == (2, 6, 2, DV)
+    np.testing.assert_allclose(got, _sdpa_ref(q, K, V, lens, scale), rtol=1e-12, atol=1e-12)
+
+
+def test_value_head_dim_of_its_own_brute_force():
+    """Pure-Python loops, K rows of 64 dims and V rows of 32: out[d] for d < DV only."""
+    q, K, V, lens = _tiny(16, B=1, HQ=2, HK=1, D=64, DV=32, N=1, lens=(7,))
+    got = attention.decode_attention(q, K, V, lens, 0.2)
+    for h in range(2):
+        z = [0.2 * sum(q[0, h, 0, d] * K[0][t, 0, d] for d in range(64)) for t in range(7)]
+        e = [math.exp(zz - max(z)) for zz in z]
+        for d in range(32):
+            want = sum(e[t] * V[0][t, 0, d] for t in range(7)) / sum(e)
+            assert abs(got[0, h, 0, d] - want) <= 1e-12 * max(1.0, abs(want))
 
 
 def test_brute_force_python_loops():
@@ -102,11 +127,13 @@ def test_split_merge_equals_two_pass(part):
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
 
 
-@pytest.mark.parametrize("wl,bs", [("c3", 16), ("c3", 32), ("c2", 16), ("c4_2", 16)])
-def test_paged_equals_contiguous(wl, bs):
+@pytest.mark.parametrize("wl,bs,dv", [("c3", 16, None), ("c3", 32, None), ("c2", 16, None), ("c4_2", 16, None),
+                                      ("c3", 16, 64), ("c2", 16, 256), ("c4_8", 16, 256)])
+def test_paged_equals_contiguous(wl, bs, dv):
     """The same rows in a shuffled pool of small blocks and in one contiguous block per
-    sequence give identical planes after the gather, hence identical attention, bit for bit."""
-    w = make_workload(wl, B=3, len_lo=40, len_hi=100, BS=bs, HK=2, D=128)
+    sequence give identical planes after the gather, hence identical attention, bit for bit
+    (also with V rows of a head dim of their own)."""
+    w = make_workload(wl, B=3, len_lo=40, len_hi=100, BS=bs, HK=2, D=128, DV=dv)
     pool = attention.workload_pool(w)
     q = attention.q_f64(w.q_bits)
     Kp, Vp, Kc, Vc = [], [], [], []
@@ -115,17 +142,26 @@ def test_paged_equals_contiguous(wl, bs):
         k, v = w.kv(b)
         if w.bits == 16:
             assert np.array_equal(g["k"], k.transpose(1, 0, 2))
+            assert np.array_equal(g["v"], v.transpose(1, 0, 2))
         else:
-            words, s, bb = quant.quantize(k, w.bits)
-            assert np.array_equal(g["k"], words.transpose(1, 0, 2))
-            assert np.array_equal(g["k_scale"], s.transpose(1, 0, 2))
-            assert np.array_equal(g["k_bias"], bb.transpose(1, 0, 2))
+            for name, x in (("k", k), ("v", v)):
+                words, s, bb = quant.quantize(x, w.bits)
+                assert np.array_equal(g[name], words.transpose(1, 0, 2))
+                assert np.array_equal(g[name + "_scale"], s.transpose(1, 0, 2))
+                assert np.array_equal(g[name + "_bias"], bb.transpose(1, 0, 2))
+        assert vc_width(g, w) == w.DV
         kp, vp = pool.dequantized(w.table[b], int(w.lengths[b]))
         kc, vc = paged.rows_dequantized(k, v, w.bits)
         Kp.append(kp), Vp.append(vp), Kc.append(kc), Vc.append(vc)
     a = attention.decode_attention(q, Kp, Vp, w.lengths, w.scale)
     c = attention.decode_attention(q, Kc, Vc, w.lengths, w.scale)
+    assert a.shape[-1] == w.DV
     assert np.array_equal(a, c)
+
+
+def vc_width(g, w):
+    """Head dims of the gathered V rows (codes of bits each, or bf16 values)."""
+    return g["v"].shape[-1] * (1 if w.bits == 16 else 32) // (1 if w.bits == 16 else w.bits)
 
 
 def test_unwritten_slots_stay_zero_and_tail_is_not_read():

@@ -42,7 +42,7 @@ def _dequant_no_bias(words, s, b, bits, group=64):
 
 def _decode_wrong_gqa(q, K, V, lengths, scale):
     B, HQ, N, D = q.shape
-    out = np.zeros((B, HQ, N, D))
+    out = np.zeros((B, HQ, N, V[0].shape[2]))
     for b in range(B):
         L = int(lengths[b])
         HK = K[b].shape[1]
@@ -56,7 +56,7 @@ def _decode_wrong_gqa(q, K, V, lengths, scale):
 
 def _decode_off_by_one(q, K, V, lengths, scale):
     B, HQ, N, D = q.shape
-    out = np.zeros((B, HQ, N, D))
+    out = np.zeros((B, HQ, N, V[0].shape[2]))
     for b in range(B):
         L = int(lengths[b])
         HK = K[b].shape[1]
@@ -130,7 +130,9 @@ PINS = [
     (TA.test_matches_torch_sdpa, (4, 64, 3)),
     (TA.test_closed_forms, ()),
     (TA.test_split_merge_equals_two_pass, (64,)),
-    (TA.test_paged_equals_contiguous, ("c3", 16)),
+    (TA.test_paged_equals_contiguous, ("c3", 16, None)),
+    (TA.test_paged_equals_contiguous, ("c3", 16, 64)),
+    (TA.test_value_head_dim_of_its_own_matches_torch_sdpa, (4, 128, 64)),
 ]
 
 

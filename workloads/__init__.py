@@ -15,7 +15,8 @@ Recipe (numpy PCG64; every stream keyed by a SeedSequence):
   are padded with -1.
 * q: ``default_rng(SeedSequence([seed, c, 0])).standard_normal((B, HQ, N, D), f32)``.
 * sequence b: ``r = default_rng(SeedSequence([seed, c, 1 + b]))``;
-  K = ``r.standard_normal((len_b, HK, D), f32)``, then V likewise; for the
+  K = ``r.standard_normal((len_b, HK, D), f32)``, then V likewise (``(len_b, HK, DV)``; DV = D
+  unless a V head dim of its own is asked for, and the outlier channels below DV); for the
   per-token-norm workload K factors then V factors
   ``exp(r.uniform(ln 0.5, ln 4, (len_b, HK)))`` scale each row.
 * K, V and q are rounded to bf16 (round to nearest even on the f32 bit pattern).
@@ -66,6 +67,7 @@ class Spec:
     outliers: int = 0            # outlier channels per KV head, scaled x8
     token_norm: bool = False     # per-(token, head) log-uniform [0.5, 4] row factor
     group: int = 64
+    DV: int = 0                  # V head dim; 0 = D
 
 
 WORKLOADS = {
@@ -100,6 +102,7 @@ class Workload:
     BS: int
     group: int
     scale: float
+    DV: int                      # V head dim (D unless asked otherwise)
     lengths: np.ndarray          # int64 [B]
     table: np.ndarray            # int32 [B, max_blocks], -1 padded
     num_blocks: int
@@ -119,16 +122,17 @@ class Workload:
         return int(self.table.shape[1])
 
     def kv_f32(self, b: int) -> Tuple[np.ndarray, np.ndarray]:
-        """Unrounded f32 draws of sequence b's K and V rows, [len_b, HK, D]."""
+        """Unrounded f32 draws of sequence b's K [len_b, HK, D] and V [len_b, HK, DV] rows."""
         s = self.spec
         L = int(self.lengths[b])
         r = np.random.default_rng(np.random.SeedSequence([self.seed, s.key, 1 + b]))
         k = r.standard_normal((L, self.HK, self.D), dtype=np.float32)
-        v = r.standard_normal((L, self.HK, self.D), dtype=np.float32)
+        v = r.standard_normal((L, self.HK, self.DV), dtype=np.float32)
         if self.outlier_dims is not None:
             for h in range(self.HK):
                 k[:, h, self.outlier_dims[h]] *= np.float32(8.0)
-                v[:, h, self.outlier_dims[h]] *= np.float32(8.0)
+                od = self.outlier_dims[h]
+                v[:, h, od[od < self.DV]] *= np.float32(8.0)
         if s.token_norm:
             lo, hi = math.log(0.5), math.log(4.0)
             kf = np.exp(r.uniform(lo, hi, (L, self.HK))).astype(np.float32)
@@ -138,7 +142,7 @@ class Workload:
         return k, v
 
     def kv(self, b: int) -> Tuple[np.ndarray, np.ndarray]:
-        """Sequence b's K and V rows as bf16 bit patterns, uint16 [len_b, HK, D]."""
+        """Sequence b's K and V rows as bf16 bit patterns, uint16 [len_b, HK, D] and [len_b, HK, DV]."""
         k, v = self.kv_f32(b)
         return bf16_bits_from_f32(k), bf16_bits_from_f32(v)
 
@@ -150,16 +154,15 @@ class Workload:
 
     def attention_flops(self) -> int:
         """Multiply-add flops of one decode step's attention: 2 * (q.k + p.v) MACs, i.e.
-        sum(len) * HK * 2 * (2 * REP * N * D) (every cached token meets every query vector of its
+        sum(len) * HK * 2 * REP * N * (D + DV) (every cached token meets every query vector of its
         KV head; causal masking of the last N - 1 tokens is not discounted)."""
-        return int(self.lengths.sum()) * self.HK * 2 * (2 * self.REP * self.N * self.D)
+        return int(self.lengths.sum()) * self.HK * 2 * self.REP * self.N * (self.D + self.DV)
 
     def effective_bytes(self) -> int:
         """K/V bytes one decode step must read: sum(len) * HK * (K + V bytes per token row)."""
-        if self.bits == 16:
-            per = 2 * 2 * self.D
-        else:
-            per = 2 * (self.D * self.bits // 8 + 2 * 2 * (self.D // self.group))
+        def row(d):
+            return 2 * d if self.bits == 16 else d * self.bits // 8 + 2 * 2 * (d // self.group)
+        per = row(self.D) + row(self.DV)
         return int(self.lengths.sum()) * self.HK * per
 
 
@@ -167,12 +170,13 @@ def make_workload(name: str, *, B: Optional[int] = None, len_lo: Optional[int] =
                   len_hi: Optional[int] = None, BS: Optional[int] = None, seed: int = 0,
                   bits: Optional[int] = None, N: Optional[int] = None,
                   HQ: Optional[int] = None, HK: Optional[int] = None,
-                  D: Optional[int] = None, group: Optional[int] = None) -> Workload:
+                  D: Optional[int] = None, group: Optional[int] = None,
+                  DV: Optional[int] = None) -> Workload:
     """Build a named workload, optionally shrunk (fewer / shorter sequences) or reshaped for
     tests (the draws depend only on the seed, the workload's key and the shapes)."""
     s = WORKLOADS[name]
     over = {k: v for k, v in dict(B=B, len_lo=len_lo, len_hi=len_hi, BS=BS, bits=bits, N=N,
-                                   HQ=HQ, HK=HK, D=D, group=group).items() if v is not None}
+                                   HQ=HQ, HK=HK, D=D, group=group, DV=DV).items() if v is not None}
     s = dataclasses.replace(s, **over)
     rng = np.random.default_rng(np.random.SeedSequence([seed, s.key]))
     lengths = rng.integers(s.len_lo, s.len_hi + 1, size=s.B).astype(np.int64)
@@ -201,5 +205,5 @@ def make_workload(name: str, *, B: Optional[int] = None, len_lo: Optional[int] =
         q_bits = bf16_bits_from_f32(
             (q_bits.astype(np.uint32) << 16).view(np.float32) * np.float32(s.q_prescale))
     return Workload(name=name, spec=s, seed=seed, bits=s.bits, B=s.B, HQ=s.HQ, HK=s.HK, D=s.D,
-                    N=s.N, BS=bs, group=s.group, scale=s.scale, lengths=lengths, table=table,
-                    num_blocks=NB, outlier_dims=outl, q_bits=q_bits)
+                    N=s.N, BS=bs, group=s.group, scale=s.scale, DV=s.DV or s.D, lengths=lengths,
+                    table=table, num_blocks=NB, outlier_dims=outl, q_bits=q_bits)
