@@ -81,8 +81,8 @@ def cpu_baseline(w, budget_s: float):
         blas_threads = 1
     order = list(range(w.B))
     done, elapsed, eff = [], 0.0, 0
-    per = paged.quant.bytes_per_token_head(w.bits, w.D, w.group)
-    pool = paged.Pool(w.num_blocks, w.HK, w.BS, w.D, w.bits, w.group)
+    per = w.effective_bytes() // (int(w.lengths.sum()) * w.HK)          # K + V row bytes of a token
+    pool = paged.Pool(w.num_blocks, w.HK, w.BS, w.D, w.bits, w.group, v_head_dim=w.DV)
     while order and elapsed < budget_s:
         b = order.pop(0)
         k, v = w.kv(b)
@@ -122,6 +122,7 @@ def main():
     ap.add_argument("--bits", type=int, default=0, help="page format override: 16 (bf16) or 2..8 (affine)")
     ap.add_argument("--group", type=int, default=0, help="scale-group override (32, 64 or 128 head dims)")
     ap.add_argument("--rows", type=int, default=0, help="query rows per sequence override (N)")
+    ap.add_argument("--dv", type=int, default=0, help="V head dim override (DV; default the K head dim)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--engine", choices=["auto", "vector", "matrix"], default="auto",
                     help="partial-pass engine: vector ALU (the default) or matrix cores (4-bit pages)")
@@ -190,11 +191,11 @@ def main():
         return
 
     t_setup = time.time()
-    over = {k: v for k, v in (("bits", args.bits), ("group", args.group), ("N", args.rows)) if v}
+    over = {k: v for k, v in (("bits", args.bits), ("group", args.group), ("N", args.rows), ("DV", args.dv)) if v}
     w = make_workload(args.workload, **over)
-    log(f"[bench] workload {w.name}: B={w.B} HQ={w.HQ} HK={w.HK} D={w.D} N={w.N} bits={w.bits} "
+    log(f"[bench] workload {w.name}: B={w.B} HQ={w.HQ} HK={w.HK} D={w.D} DV={w.DV} N={w.N} bits={w.bits} "
         f"BS={w.BS} sum(len)={int(w.lengths.sum())} NB={w.num_blocks}")
-    pool = kvq.Pool(w.num_blocks, w.HK, w.BS, w.D, w.bits, w.group, device=dev)
+    pool = kvq.Pool(w.num_blocks, w.HK, w.BS, w.D, w.bits, w.group, device=dev, v_head_dim=w.DV)
     new_k, new_v, new_slots = [], [], []
     # the draws of each sequence are independent (own seed), so a few threads generate them
     # ahead of the device appends (NumPy's generators release the GIL)
@@ -223,14 +224,14 @@ def main():
     engine = {"auto": kvq.ENGINE_AUTO, "vector": kvq.ENGINE_VECTOR, "matrix": kvq.ENGINE_MATRIX}[args.engine]
     shape = kvq.make_shape(pool, w.B, w.HQ, w.N, w.max_blocks, w.max_len, args.partition_tokens, False, engine)
     ws = torch.empty(kvq.paged_decode_workspace_bytes(pool, shape), dtype=torch.uint8, device=dev)
-    out = torch.empty((w.B, w.HQ, w.N, w.D), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((w.B, w.HQ, w.N, w.DV), dtype=torch.bfloat16, device=dev)
     pt = kvq.paged_decode_partition_tokens(pool, shape)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
     torch.cuda.synchronize()
     log(f"[bench] setup {time.time() - t_setup:.0f} s; partition {pt} tokens; workspace {ws.numel() >> 20} MiB")
 
     kn = nk.view(w.B, w.N, w.HK, w.D)
-    vn = nv.view(w.B, w.N, w.HK, w.D)
+    vn = nv.view(w.B, w.N, w.HK, w.DV)
 
     def step(mid=None, shp=shape, wsp=ws):
         """one decode step: paged_decode_step_partial (append of the new rows with slots from the
@@ -344,7 +345,8 @@ def main():
             "hbm": hbm, "alu": alu, "kernel_source_hash": src_hash}
 
     variants = {}
-    if args.engine == "auto" and w.bits == 4 and w.group == 64 and w.D in (128, 256) and args.partition_tokens <= 0:
+    if (args.engine == "auto" and w.bits == 4 and w.group == 64 and w.D in (128, 256) and w.DV == w.D
+            and args.partition_tokens <= 0):
         # the separately flagged matrix-core engine on the same inputs, timed the same way
         shp_m = kvq.make_shape(pool, w.B, w.HQ, w.N, w.max_blocks, w.max_len, 0, False, kvq.ENGINE_MATRIX)
         ws_m = torch.empty(kvq.paged_decode_workspace_bytes(pool, shp_m), dtype=torch.uint8, device=dev)

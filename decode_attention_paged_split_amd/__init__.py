@@ -50,7 +50,8 @@ class KvqError(RuntimeError):
 class PoolDesc(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("bits", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+                ("bits", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("v_head_dim", ctypes.c_int32)]
 
 
 class DecodeShape(ctypes.Structure):
@@ -256,25 +257,29 @@ class Pool:
     planes["k"], planes["v"]: uint32 codes [NB, HK, BS, D*bits/32] (affine; a row's codes are one
     little-endian bit stream, so 3/5/6-bit codes straddle words) or bf16 bit
     patterns as int16 [NB, HK, BS, D] (bits == 16); planes["{k,v}_{scale,bias}"]: bf16
-    bit patterns as int16 [NB, HK, BS, D/64].
+    bit patterns as int16 [NB, HK, BS, D/group_size].  The V planes take v_head_dim (DV,
+    default head_dim) in place of D.
     """
 
     def __init__(self, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
-                 bits: int, group_size: int = 64, device=None):
+                 bits: int, group_size: int = 64, device=None, v_head_dim: Optional[int] = None):
         import torch
-        self.desc = PoolDesc(num_blocks, num_kv_heads, block_size, head_dim, bits, group_size)
+        dv = head_dim if v_head_dim is None else v_head_dim
+        self.desc = PoolDesc(num_blocks, num_kv_heads, block_size, head_dim, bits, group_size, dv)
         dev = torch.device(device) if device is not None else torch.device("cuda")
         shape = lambda w: (num_blocks, num_kv_heads, block_size, w)  # noqa: E731
         if bits == 16:
             self.planes = {"k": torch.zeros(shape(head_dim), dtype=torch.int16, device=dev),
-                           "v": torch.zeros(shape(head_dim), dtype=torch.int16, device=dev)}
+                           "v": torch.zeros(shape(dv), dtype=torch.int16, device=dev)}
         else:
             W, G = head_dim * bits // 32, head_dim // group_size
+            WV, GV = dv * bits // 32, dv // group_size
             # uint32 codes held as int32 storage (torch has no uint32 arithmetic on every backend)
             self.planes = {"k": torch.zeros(shape(W), dtype=torch.int32, device=dev),
-                           "v": torch.zeros(shape(W), dtype=torch.int32, device=dev)}
+                           "v": torch.zeros(shape(WV), dtype=torch.int32, device=dev)}
             for n in PLANES[2:]:
-                self.planes[n] = torch.zeros(shape(G), dtype=torch.int16, device=dev)
+                self.planes[n] = torch.zeros(shape(GV if n.startswith("v") else G), dtype=torch.int16,
+                                             device=dev)
         ptrs = [self.planes[n].data_ptr() if n in self.planes else 0 for n in PLANES]
         for i, n in enumerate(PLANES):
             if n in self.planes:
@@ -286,6 +291,10 @@ class Pool:
     @property
     def bits(self) -> int:
         return self.desc.bits
+
+    @property
+    def v_head_dim(self) -> int:
+        return self.desc.v_head_dim
 
     def append(self, k, v, slots, stream=None) -> None:
         kv_append_quantize(self, k, v, slots, stream)
@@ -312,10 +321,12 @@ def decode(q, pool: Pool, block_table, lengths, scale: float, max_len: int, part
     """Allocate (if not given) workspace and output, then run paged_decode_attention.
 
     q: bf16 [B, HQ, N, D] (torch.bfloat16 or int16 bit patterns); block_table int32 [B, M];
-    lengths int32 [B].  Returns out [B, HQ, N, D] (bfloat16, or float32 if out_f32).
+    lengths int32 [B].  Returns out [B, HQ, N, DV] (bfloat16, or float32 if out_f32; DV the pool's
+    V head dim).
     """
     import torch
-    B, HQ, N, D = q.shape
+    B, HQ, N, _ = q.shape
+    D = pool.v_head_dim
     shape = make_shape(pool, B, HQ, N, block_table.shape[1], max_len, partition_tokens, out_f32, engine)
     if workspace is None:
         workspace = torch.empty(paged_decode_workspace_bytes(pool, shape), dtype=torch.uint8,
@@ -331,10 +342,11 @@ def decode_step(q, k_new, v_new, pool: Pool, block_table, lengths, scale: float,
                 partition_tokens: int = 0, out_f32: bool = False, workspace=None, out=None, stream=None,
                 engine: int = ENGINE_AUTO):
     """paged_decode_step with freshly allocated workspace and output (if not given): append the
-    step's new rows k_new, v_new ([B, N, HK, D] bf16) at the slots their positions take in the
-    block table, then attend.  Returns out [B, HQ, N, D]."""
+    step's new rows k_new ([B, N, HK, D] bf16) and v_new ([B, N, HK, DV]) at the slots their
+    positions take in the block table, then attend.  Returns out [B, HQ, N, DV]."""
     import torch
-    B, HQ, N, D = q.shape
+    B, HQ, N, _ = q.shape
+    D = pool.v_head_dim
     shape = make_shape(pool, B, HQ, N, block_table.shape[1], max_len, partition_tokens, out_f32, engine)
     if workspace is None:
         workspace = torch.empty(paged_decode_workspace_bytes(pool, shape), dtype=torch.uint8,

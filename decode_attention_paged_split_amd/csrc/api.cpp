@@ -45,6 +45,9 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 int plane_count(int bits) { return bits == 16 ? 2 : 6; }
 
+// the V rows' head dim (0 in a descriptor stands for head_dim)
+int v_dim(const kvq_pool_desc* d) { return d->v_head_dim ? d->v_head_dim : d->head_dim; }
+
 int validate_desc(const kvq_pool_desc* d) {
   if (!d) return fail(KVQ_ERR_INVALID, "pool descriptor is NULL");
   if (d->num_blocks < 1 || d->num_kv_heads < 1 || d->block_size < 1 || d->head_dim < 1)
@@ -60,6 +63,12 @@ int validate_desc(const kvq_pool_desc* d) {
                 d->bits, d->head_dim, d->head_dim * d->bits / 8);
   if (!(d->group_size == 32 || d->group_size == 64 || d->group_size == 128) || d->head_dim % d->group_size != 0)
     return fail(KVQ_ERR_UNSUPPORTED, "group_size must be 32, 64 or 128 and divide head_dim, got %d", d->group_size);
+  const int dv = v_dim(d);
+  if (d->v_head_dim < 0) return fail(KVQ_ERR_INVALID, "v_head_dim must be >= 0 (0: head_dim), got %d", d->v_head_dim);
+  if (dv != d->head_dim && !kvq::valu_dv_ok(d->bits, d->head_dim, dv, d->group_size))
+    return fail(KVQ_ERR_UNSUPPORTED,
+                "v_head_dim %d with head_dim %d: a V head dim of its own must be head_dim / 2 or 2 * head_dim "
+                "within 64..256, on bf16, 8-, 4- or 2-bit pages with group_size 64", dv, d->head_dim);
   const size_t rows = (size_t)d->num_blocks * d->num_kv_heads * d->block_size;
   if (rows >= (size_t)1 << 31)
     return fail(KVQ_ERR_UNSUPPORTED, "num_blocks * num_kv_heads * block_size must stay below 2^31 rows");
@@ -67,9 +76,11 @@ int validate_desc(const kvq_pool_desc* d) {
 }
 
 size_t plane_row_bytes(const kvq_pool_desc* d, int plane) {
-  if (d->bits == 16) return (plane <= KVQ_PLANE_V) ? (size_t)d->head_dim * 2 : 0;
-  if (plane <= KVQ_PLANE_V) return (size_t)d->head_dim * d->bits / 8;
-  if (plane < KVQ_NUM_PLANES) return (size_t)(d->head_dim / d->group_size) * 2;
+  const bool vp = plane == KVQ_PLANE_V || plane == KVQ_PLANE_V_SCALE || plane == KVQ_PLANE_V_BIAS;
+  const size_t dim = (size_t)(vp ? v_dim(d) : d->head_dim);
+  if (d->bits == 16) return (plane <= KVQ_PLANE_V) ? dim * 2 : 0;
+  if (plane <= KVQ_PLANE_V) return dim * d->bits / 8;
+  if (plane < KVQ_NUM_PLANES) return (dim / d->group_size) * 2;
   return 0;
 }
 
@@ -90,8 +101,8 @@ int device_cus() {
 constexpr int MAX_PARTS = 8192;
 
 // query vectors per workgroup: the largest power of two <= kvq::valu_max_qvw dividing REP * N
-int qvw_for(int qv, int bits, int D, int gs) {
-  for (int w = kvq::valu_max_qvw(bits, D, gs); w >= 1; w /= 2)
+int qvw_for(int qv, int bits, int D, int DV, int gs) {
+  for (int w = kvq::valu_max_qvw(bits, D, DV, gs); w >= 1; w /= 2)
     if (qv % w == 0) return w;
   return 1;
 }
@@ -148,7 +159,7 @@ int qvw_of(const kvq_pool* pool, const kvq_decode_shape* s) {
   const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
   if (use_mfma(s))
     return (pool->desc.head_dim == 256 && qv <= kvq::MFMA_PAIR_QVW) ? kvq::MFMA_PAIR_QVW : kvq::MFMA_QVW;
-  return qvw_for(qv, pool->desc.bits, pool->desc.head_dim, pool->desc.group_size);
+  return qvw_for(qv, pool->desc.bits, pool->desc.head_dim, pool->desc.v_head_dim, pool->desc.group_size);
 }
 
 int qgroups_of(const kvq_pool* pool, const kvq_decode_shape* s) {
@@ -184,23 +195,24 @@ int validate_shape(const kvq_pool* pool, const kvq_decode_shape* s) {
   const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
   if (s->engine < KVQ_ENGINE_AUTO || s->engine > KVQ_ENGINE_MATRIX)
     return fail(KVQ_ERR_INVALID, "engine must be 0 (automatic), 1 (vector ALU) or 2 (matrix cores)");
+  const kvq_pool_desc& pd = pool->desc;
   if (use_mfma(s)) {
-    if (!kvq::mfma_supported(pool->desc.bits, pool->desc.head_dim, pool->desc.group_size))
-      return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core engine reads 4-bit pages with head_dim 128 or 256 and "
-                                       "group_size 64");
+    if (!kvq::mfma_supported(pd.bits, pd.head_dim, pd.group_size) || pd.v_head_dim != pd.head_dim)
+      return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core engine reads 4-bit pages with head_dim 128 or 256 "
+                                       "(v_head_dim the same) and group_size 64");
     if (pt > 0)
       return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core engine runs the balanced stream schedule only "
                                        "(partition_tokens 0 or -1)");
-  } else if (!kvq::partial_supported(pool->desc.bits, pool->desc.head_dim, pool->desc.group_size,
-                                     qvw_for(qv, pool->desc.bits, pool->desc.head_dim, pool->desc.group_size))) {
-    return fail(KVQ_ERR_UNSUPPORTED, "no kernel for bits=%d D=%d", pool->desc.bits, pool->desc.head_dim);
+  } else if (!kvq::partial_supported(pd.bits, pd.head_dim, pd.v_head_dim, pd.group_size,
+                                     qvw_for(qv, pd.bits, pd.head_dim, pd.v_head_dim, pd.group_size))) {
+    return fail(KVQ_ERR_UNSUPPORTED, "no kernel for bits=%d D=%d DV=%d", pd.bits, pd.head_dim, pd.v_head_dim);
   }
   return KVQ_OK;
 }
 
 // Partials: fixed partitions hold [B, HQ, N, parts] rows; the stream schedule holds
-// (ranges + units) * sub slots of QVW vectors (slot = (unit + range) * sub + wave in range).  Each partial row is D floats of
-// unnormalised output plus (max, normaliser).  The vector engine adds its copy of q in the
+// (ranges + units) * sub slots of QVW vectors (slot = (unit + range) * sub + wave in range).  Each partial row is DV
+// floats of unnormalised output (DV: the V head dim) plus (max, normaliser).  The vector engine adds its copy of q in the
 // codes' pair order, D/32 blocks of Q_BLOCK_WORDS words per query vector.
 struct WsLayout {
   size_t ml_off, qp_off, total;
@@ -218,7 +230,7 @@ WsLayout workspace_layout(const kvq_pool* pool, const kvq_decode_shape* s, int p
   }
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   WsLayout L{};
-  L.ml_off = up(rows * pool->desc.head_dim * sizeof(float));
+  L.ml_off = up(rows * pool->desc.v_head_dim * sizeof(float));
   L.qp_off = L.total = L.ml_off + rows * 2 * sizeof(float);
   if (!use_mfma(s)) {
     const size_t qv = (size_t)s->batch * pool->desc.num_kv_heads * qgroups_of(pool, s) * qvw_of(pool, s);
@@ -335,6 +347,7 @@ int kv_pool_create(const kvq_pool_desc* desc, kvq_pool** out) {
   if (int r = validate_desc(desc)) return r;
   kvq_pool* p = new kvq_pool();
   p->desc = *desc;
+  p->desc.v_head_dim = v_dim(desc);
   p->owned = true;
   for (int i = 0; i < KVQ_NUM_PLANES; ++i) {
     p->planes[i] = nullptr;
@@ -364,6 +377,7 @@ int kv_pool_wrap(const kvq_pool_desc* desc, void* const planes[KVQ_NUM_PLANES], 
   if (!planes) return fail(KVQ_ERR_INVALID, "planes is NULL");
   kvq_pool* p = new kvq_pool();
   p->desc = *desc;
+  p->desc.v_head_dim = v_dim(desc);
   p->owned = false;
   for (int i = 0; i < KVQ_NUM_PLANES; ++i) {
     p->bytes[i] = kv_pool_plane_bytes(desc, i);
@@ -415,7 +429,8 @@ int kv_append_quantize(kvq_pool* pool, const uint16_t* k, const uint16_t* v, con
   a.k_plane = pool->planes[KVQ_PLANE_K]; a.v_plane = pool->planes[KVQ_PLANE_V];
   a.k_scale = pool->planes[KVQ_PLANE_K_SCALE]; a.k_bias = pool->planes[KVQ_PLANE_K_BIAS];
   a.v_scale = pool->planes[KVQ_PLANE_V_SCALE]; a.v_bias = pool->planes[KVQ_PLANE_V_BIAS];
-  a.T = num_tokens; a.HK = d.num_kv_heads; a.D = d.head_dim; a.BS = d.block_size; a.group = d.group_size;
+  a.T = num_tokens; a.HK = d.num_kv_heads; a.D = d.head_dim; a.Dv = d.v_head_dim; a.BS = d.block_size;
+  a.group = d.group_size;
   a.num_slots = (int64_t)d.num_blocks * d.block_size;
   hipError_t e = kvq::launch_append(a, d.bits, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");
@@ -444,8 +459,8 @@ struct Plan {
 hipError_t launch_plan_partial(const Plan& P, const kvq_pool* pool, int B, hipStream_t st, bool q_ready = false) {
   return timed(KVQ_TIMING_PARTIAL, st, [&] {
     if (P.mfma) return kvq::launch_partial_mfma(P.a, pool->desc.head_dim, st);
-    return kvq::launch_partial(P.a, pool->desc.bits, pool->desc.head_dim, pool->desc.group_size, P.qvw, B, q_ready,
-                               st);
+    return kvq::launch_partial(P.a, pool->desc.bits, pool->desc.head_dim, pool->desc.v_head_dim,
+                               pool->desc.group_size, P.qvw, B, q_ready, st);
   });
 }
 
@@ -498,7 +513,7 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   kvq::MergeArgs& m = P->m;
   m = kvq::MergeArgs{};
   m.opart = a.opart; m.ml = a.ml; m.lengths = lengths; m.out = out;
-  m.HQ = shape->num_q_heads; m.N = shape->q_rows; m.D = d.head_dim; m.part_tokens = pt;
+  m.HQ = shape->num_q_heads; m.N = shape->q_rows; m.D = d.v_head_dim; m.part_tokens = pt;
   m.num_parts = parts; m.out_f32 = shape->out_f32 ? 1 : 0; m.max_len = shape->max_len;
   m.len_cap = a.len_cap;
   m.batch = shape->batch; m.HK = d.num_kv_heads; m.qgroups = a.qgroups; m.qvw = P->qvw;
@@ -562,12 +577,13 @@ int step_partial(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new
   ap.k_plane = pool->planes[KVQ_PLANE_K]; ap.v_plane = pool->planes[KVQ_PLANE_V];
   ap.k_scale = pool->planes[KVQ_PLANE_K_SCALE]; ap.k_bias = pool->planes[KVQ_PLANE_K_BIAS];
   ap.v_scale = pool->planes[KVQ_PLANE_V_SCALE]; ap.v_bias = pool->planes[KVQ_PLANE_V_BIAS];
-  ap.T = shape->batch * shape->q_rows; ap.HK = d.num_kv_heads; ap.D = d.head_dim; ap.BS = d.block_size;
-  ap.group = d.group_size;
+  ap.T = shape->batch * shape->q_rows; ap.HK = d.num_kv_heads; ap.D = d.head_dim; ap.Dv = d.v_head_dim;
+  ap.BS = d.block_size; ap.group = d.group_size;
   ap.num_slots = (int64_t)d.num_blocks * d.block_size;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = timed(KVQ_TIMING_PREP, st, [&] {
-    return kvq::launch_step_prep(ap, P.a, d.bits, d.head_dim, d.group_size, P.qvw, !P.mfma, shape->batch, st);
+    return kvq::launch_step_prep(ap, P.a, d.bits, d.head_dim, d.v_head_dim, d.group_size, P.qvw, !P.mfma,
+                                 shape->batch, st);
   });
   if (e != hipSuccess) return hip_fail(e, "step launch");
   e = launch_plan_partial(P, pool, shape->batch, st, true);

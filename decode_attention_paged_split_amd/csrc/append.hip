@@ -2,6 +2,8 @@
 // arithmetic (quantizer reading, packing, mapping) is in append_rows.hpp.
 #include "append_rows.hpp"
 
+#include <algorithm>
+
 namespace kvq {
 
 template <int BITS, int GS>
@@ -26,7 +28,7 @@ static hipError_t launch_append_g(const AppendArgs& a, dim3 grid, hipStream_t st
 
 hipError_t launch_append(const AppendArgs& a, int bits, hipStream_t stream) {
   const int ept = append_ept(bits);
-  const int64_t total = (int64_t)a.T * a.HK * (a.D / ept);
+  const int64_t total = (int64_t)a.T * a.HK * (std::max(a.D, a.Dv) / ept);
   if (total == 0) return hipSuccess;
   const int block = 256;
   const int64_t grid = (total + block - 1) / block;

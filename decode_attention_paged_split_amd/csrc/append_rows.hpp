@@ -45,13 +45,14 @@ __device__ __forceinline__ int64_t decode_slot(const AppendArgs& a, int64_t tok)
   return (int64_t)phys * a.BS + t % a.BS;
 }
 
-// one thread per EPT elements of one (token, head) row; gid indexes (token, head, chunk); GS is
-// the scale-group size (affine pages; bf16 rows ignore it)
+// one thread per EPT elements of one (token, head) row; gid indexes (token, head, chunk) with
+// chunks over the wider of the K row (D) and the V row (Dv); GS is the scale-group size (affine
+// pages; bf16 rows ignore it)
 template <int BITS, int GS>
 __device__ __forceinline__ void append_rows(const AppendArgs& a, int64_t gid) {
   constexpr int EPT = append_ept(BITS);         // elements per thread
   constexpr int TPG = GS / EPT;                 // threads per scale group
-  const int chunks = a.D / EPT;
+  const int chunks = max(a.D, a.Dv) / EPT;
   const int64_t total = (int64_t)a.T * a.HK * chunks;
   const bool live = gid < total;
   const int64_t g = live ? gid : 0;
@@ -67,18 +68,23 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int64_t gid) {
   const int64_t prow = (phys * a.HK + head) * a.BS + off;   // row index within a plane
 
   for (int kv = 0; kv < 2; ++kv) {
+    // this pass's row width; chunks beyond it (the narrower of K and V) are whole scale groups
+    // that load and store nothing
+    const int dk = kv ? a.Dv : a.D;
+    const bool on = live && chunk * EPT < dk;
+    const bool put = store && on;
     const uint16_t* src = kv ? a.v : a.k;
-    const uint4* s4 = reinterpret_cast<const uint4*>(src + row * a.D + chunk * EPT);
+    const uint4* s4 = reinterpret_cast<const uint4*>(src + row * dk + chunk * EPT);
     uint32_t w[EPT / 2];
 #pragma unroll
     for (int q = 0; q < EPT / 8; ++q) {
-      const uint4 x = live ? s4[q] : make_uint4(0, 0, 0, 0);
+      const uint4 x = on ? s4[q] : make_uint4(0, 0, 0, 0);
       w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
     }
     if constexpr (BITS == 16) {
-      if (store) {
+      if (put) {
         uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(kv ? a.v_plane : a.k_plane) +
-                                              prow * a.D + chunk * EPT);
+                                              prow * dk + chunk * EPT);
         dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       }
       continue;
@@ -118,13 +124,13 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int64_t gid) {
         out[wj] |= c[i] << sh;
         if (sh + BITS > 32) out[wj + 1] |= c[i] >> (32 - sh);   // a code straddling two words
       }
-      if (store) {
-        const int W = a.D * BITS / 32;
+      if (put) {
+        const int W = dk * BITS / 32;
         uint32_t* dst = static_cast<uint32_t*>(kv ? a.v_plane : a.k_plane) + prow * W + chunk * NWORDS;
 #pragma unroll
         for (int j = 0; j < NWORDS; ++j) dst[j] = out[j];
         if ((chunk % TPG) == 0) {
-          const int G = a.D / GS;
+          const int G = dk / GS;
           const int grp = chunk / TPG;
           uint16_t* sp = static_cast<uint16_t*>(kv ? a.v_scale : a.k_scale);
           uint16_t* bp = static_cast<uint16_t*>(kv ? a.v_bias : a.k_bias);

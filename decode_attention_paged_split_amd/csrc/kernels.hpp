@@ -8,7 +8,7 @@ namespace kvq {
 
 struct AppendArgs {
   const uint16_t* k;      // [T, HK, D] bf16
-  const uint16_t* v;
+  const uint16_t* v;      // [T, HK, Dv] bf16
   const int64_t* slots;   // [T]; NULL: a decode step's new rows, slots from the block table
   const int32_t* table;   // decode step: [B, max_blocks] block table
   const int32_t* lengths; // decode step: [B], counting the N new rows
@@ -20,6 +20,7 @@ struct AppendArgs {
   void* v_scale;
   void* v_bias;
   int32_t T, HK, D, BS;
+  int32_t Dv;             // V head dim
   int32_t group;          // scale-group size (affine pages)
   int64_t num_slots;      // num_blocks * BS
 };
@@ -43,7 +44,7 @@ struct PartialArgs {
   const uint16_t* vb;
   const int32_t* table;     // [B, max_blocks]
   const int32_t* lengths;   // [B]
-  float* opart;             // [B, HQ, N, P, D] f32, unnormalised
+  float* opart;             // [B, HQ, N, P, DV] f32, unnormalised (DV: the V head dim)
   float* ml;                // [B, HQ, N, P, 2] f32: running max (log2 units), normaliser
   uint32_t* qp;             // vector engine: [units, D/32 blocks x QVW, Q_BLOCK_WORDS] q in the codes' order
   float scale_log2e;        // softmax scale * log2(e)
@@ -62,7 +63,7 @@ struct MergeArgs {
   const float* opart;
   const float* ml;
   const int32_t* lengths;
-  void* out;                // [B, HQ, N, D] bf16 or f32
+  void* out;                // [B, HQ, N, D] bf16 or f32 (D: the V head dim)
   int32_t HQ, N, D, part_tokens, num_parts, out_f32, max_len;
   int32_t len_cap;          // min(max_len, max_blocks * BS): lengths are clamped to [0, len_cap]
   int32_t batch, HK, qgroups, qvw, num_ranges, range_sub, min_tokens;   // stream (part_tokens == 0)
@@ -80,20 +81,31 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 
 // qvw: query vectors per workgroup (REP * N split into qgroups groups of qvw)
 // q_ready: the vector engine's q copy is already in the workspace (decode step); gs: the pool's
-// scale-group size (affine pages)
-hipError_t launch_partial(const PartialArgs& a, int bits, int D, int gs, int qvw, int B, bool q_ready,
+// scale-group size (affine pages); D, DV: the K and V head dims
+hipError_t launch_partial(const PartialArgs& a, int bits, int D, int DV, int gs, int qvw, int B, bool q_ready,
                           hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t stream);
 // decode step: the new rows' append (slots from the block table) and, for the vector engine, the
 // q copy, in one launch
-hipError_t launch_step_prep(const AppendArgs& ap, const PartialArgs& a, int bits, int D, int gs, int qvw,
+hipError_t launch_step_prep(const AppendArgs& ap, const PartialArgs& a, int bits, int D, int DV, int gs, int qvw,
                             bool vector_q, int B, hipStream_t stream);
-bool partial_supported(int bits, int D, int gs, int qvw);
+bool partial_supported(int bits, int D, int DV, int gs, int qvw);
+// a V head dim other than K's: the vector engine reads DV = D / 2 or 2 D (within 64..256) for
+// bf16, 8-, 4- and 2-bit pages with 64-element scale groups
+constexpr bool valu_dv_ok(int bits, int D, int DV, int gs) {
+  return DV == D || ((bits == 16 || ((bits == 8 || bits == 4 || bits == 2) && gs == 64)) &&
+                     (2 * DV == D || DV == 2 * D) && DV >= 64 && DV <= 256 && D >= 64 && D <= 256);
+}
 // most query vectors one wave of the vector engine carries: 8, or 4 where a V lane owns 16 head
 // dims (2-bit pages; bf16, 8-, 6- and 5-bit pages at head dim 256, whose rows take two parts) or
 // a row has 8 scale groups (the per-lane bias sums, vectors x groups, stay within 32 registers)
 constexpr int valu_max_qvw(int bits, int D, int gs) {
   return (bits == 2 || (D == 256 && bits >= 5) || (bits != 16 && D / gs > 4)) ? 4 : 8;
+}
+// the same for K rows of D and V rows of DV dims: the smaller of the two
+constexpr int valu_max_qvw(int bits, int D, int DV, int gs) {
+  return valu_max_qvw(bits, D, gs) < valu_max_qvw(bits, DV, gs) ? valu_max_qvw(bits, D, gs)
+                                                                : valu_max_qvw(bits, DV, gs);
 }
 // a row layout the vector engine reads: whole 16-byte chunks
 constexpr bool valu_row_ok(int bits, int D) { return (D * bits / 8) % 16 == 0; }

@@ -2,6 +2,6 @@
 #include "partial_valu_impl.hpp"
 
 namespace kvq {
-template hipError_t launch_valu_bits<16>(const PartialArgs&, int, int, int, int, bool, hipStream_t);
+template hipError_t launch_valu_bits<16>(const PartialArgs&, int, int, int, int, int, bool, hipStream_t);
 template hipError_t launch_step_bits<16>(const AppendArgs&, const PartialArgs&, int, int, int, bool, int, hipStream_t);
 }  // namespace kvq

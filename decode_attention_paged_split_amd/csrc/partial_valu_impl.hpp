@@ -253,20 +253,20 @@ __device__ __forceinline__ float rows_sum(float x) {
 
 // per-wave LDS of the tile engine: the tile's weights p * s_v, [token][group][vector] (each
 // token's row padded by 4 words, so the 64 lanes' row writes spread over all banks), and one
-// part of the tile's V rows
-template <int BITS, int D, int QVW, int GS>
+// part of the tile's V rows (V rows of DV head dims)
+template <int BITS, int DV, int QVW, int GS>
 struct WaveScratch {
-  static constexpr int WPITCH = Geo<BITS, D, GS>::WG * QVW + 4;
+  static constexpr int WPITCH = Geo<BITS, DV, GS>::WG * QVW + 4;
   float w[PV_TILE][WPITCH];
-  uint8_t v[PV_TILE][Geo<BITS, D, GS>::VPITCH];
+  uint8_t v[PV_TILE][Geo<BITS, DV, GS>::VPITCH];
   __device__ float* wrow(int t, int g) { return &w[t][g * QVW]; }
 };
 
-// running state of one wave over one range of one unit
-template <int BITS, int D, int QVW, int GS>
+// running state of one wave over one range of one unit (V rows of DV head dims)
+template <int BITS, int DV, int QVW, int GS>
 struct Acc {
-  float o[QVW][Geo<BITS, D, GS>::NP][Geo<BITS, D, GS>::VDPL];  // V lanes: sum_t p * code (or value)
-  float pb[QVW][Geo<BITS, D, GS>::G];         // token lanes: this lane's share of sum_t p * b_v
+  float o[QVW][Geo<BITS, DV, GS>::NP][Geo<BITS, DV, GS>::VDPL];  // V lanes: sum_t p * code (or value)
+  float pb[QVW][Geo<BITS, DV, GS>::G];        // token lanes: this lane's share of sum_t p * b_v
   float l[QVW];                           // token lanes: this lane's share of sum_t p
   float m[QVW];                           // wave-uniform running max (log2 units)
 };
@@ -276,9 +276,9 @@ struct Unit {
   int64_t u;                              // unit index (b * HK + hk) * qgroups + qg
 };
 
-template <int BITS, int D, int QVW, int GS>
-__device__ __forceinline__ void acc_init(Acc<BITS, D, QVW, GS>& st) {
-  using Gm = Geo<BITS, D, GS>;
+template <int BITS, int DV, int QVW, int GS>
+__device__ __forceinline__ void acc_init(Acc<BITS, DV, QVW, GS>& st) {
+  using Gm = Geo<BITS, DV, GS>;
 #pragma unroll
   for (int j = 0; j < QVW; ++j) {
 #pragma unroll
@@ -292,10 +292,11 @@ __device__ __forceinline__ void acc_init(Acc<BITS, D, QVW, GS>& st) {
   }
 }
 
-// the tile's per-token scale-plane entries: G bf16 each of k scale, k bias, v scale, v bias
-template <int G>
+// the tile's per-token scale-plane entries: G bf16 each of k scale and k bias, GV each of v
+// scale and v bias
+template <int G, int GV>
 struct Scales {
-  uint32_t ks[(G + 1) / 2], kb[(G + 1) / 2], vs[(G + 1) / 2], vb[(G + 1) / 2];
+  uint32_t ks[(G + 1) / 2], kb[(G + 1) / 2], vs[(GV + 1) / 2], vb[(GV + 1) / 2];
 };
 
 template <int G>
@@ -339,13 +340,15 @@ __device__ __forceinline__ RowPart<KCP> load_row_part(const char* plane, int row
 // token of the next tile this wave takes (>= t1: none left), valid in lane 0 at least; it is
 // called one tile ahead and read (made uniform) only a tile later, so an atomic behind it has a
 // whole tile to return and its wait does not hold up the loads issued after it.
-template <int BITS, int D, int QVW, int GS, class Grab>
+template <int BITS, int D, int DV, int QVW, int GS, class Grab>
 __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, int t1, Grab grab,
-                                          WaveScratch<BITS, D, QVW, GS>& ws, Acc<BITS, D, QVW, GS>& st, int lane) {
-  using Gm = Geo<BITS, D, GS>;
+                                          WaveScratch<BITS, DV, QVW, GS>& ws, Acc<BITS, DV, QVW, GS>& st, int lane) {
+  using Gm = Geo<BITS, D, GS>;                                    // K rows
+  using Gv = Geo<BITS, DV, GS>;                                   // V rows
   constexpr int ROWB = Gm::ROWB, G = Gm::G, NP = Gm::NP, KCP = Gm::KCP, GPP = Gm::GPP, NHB = Gm::NHB;
-  constexpr int PPW = Gm::PPW, WPH = Gm::WPH, VW = Gm::VW, VLPR = Gm::VLPR, VRPL = Gm::VRPL;
-  constexpr int VDPL = Gm::VDPL, NBV = Gm::NBV, KPB = Gm::KPB;
+  constexpr int PPW = Gm::PPW, WPH = Gm::WPH, KPB = Gm::KPB;
+  constexpr int VW = Gv::VW, VLPR = Gv::VLPR, VRPL = Gv::VRPL, VDPL = Gv::VDPL, NBV = Gv::NBV;
+  constexpr int GV = Gv::G, NPV = Gv::NP, KCPV = Gv::KCP, ROWBV = Gv::ROWB, KPBV = Gv::KPB;
   constexpr bool AFF = Gm::AFF;
   constexpr int QBS = Q_BLOCK_WORDS;                              // words per q block
   int tt = uni(grab());
@@ -376,25 +379,25 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
     phys = min(max(phys, 0), a.num_blocks - 1);                   // a bad entry cannot fault
     return (phys * a.HK + hk) * a.BS + (t - blk * a.BS);
   };
-  auto load_scales = [&](int row, Scales<G>& sc) {
+  auto load_scales = [&](int row, Scales<G, GV>& sc) {
     if constexpr (AFF) {
       load_plane_row<G>(a.ks, row, sc.ks);
       load_plane_row<G>(a.kb, row, sc.kb);
-      load_plane_row<G>(a.vs, row, sc.vs);
-      load_plane_row<G>(a.vb, row, sc.vb);
+      load_plane_row<GV>(a.vs, row, sc.vs);
+      load_plane_row<GV>(a.vb, row, sc.vb);
     }
   };
-  auto stage_v = [&](const RowPart<KCP>& src) {                  // this lane's V row part -> LDS
+  auto stage_v = [&](const RowPart<KCPV>& src) {                 // this lane's V row part -> LDS
 #pragma unroll
-    for (int c = 0; c < KCP; ++c) *reinterpret_cast<u32x4*>(&ws.v[lane][16 * c]) = src.c[c];
+    for (int c = 0; c < KCPV; ++c) *reinterpret_cast<u32x4*>(&ws.v[lane][16 * c]) = src.c[c];
   };
 
   // ---- prologue: rows, K and V part 0 and scales of the first tile
   int row = row_of(min(tt + lane, t1 - 1), table_entry(min(tt + lane, t1 - 1)));
   RowPart<KCP> kcur = load_row_part<KCP>(kplane, row, ROWB, 0);
-  Scales<G> sc, scn;
+  Scales<G, GV> sc, scn;
   load_scales(row, sc);
-  RowPart<KCP> vcur = load_row_part<KCP>(vplane, row, ROWB, 0);
+  RowPart<KCPV> vcur = load_row_part<KCPV>(vplane, row, ROWBV, 0);
 
   while (true) {
     const int tn = uni(tn_raw);
@@ -480,11 +483,11 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
     // (spills, 7 % slower); it reloads the current rows instead (valid addresses, never used).
     stage_v(vcur);
     const int row_next = has_next ? row_of(t_next, tbl_next) : row;
-    constexpr bool RELOAD = BITS == 4 && D == 256 && QVW == 8;
+    constexpr bool RELOAD = BITS == 4 && D == 256 && DV == 256 && QVW == 8;
     if (RELOAD || has_next) {
       kcur = load_row_part<KCP>(kplane, row_next, ROWB, 0);
       load_scales(row_next, scn);
-      vcur = load_row_part<KCP>(vplane, row_next, ROWB, 0);
+      vcur = load_row_part<KCPV>(vplane, row_next, ROWBV, 0);
     }
 
     // ---- softmax, one token per lane
@@ -506,9 +509,9 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
         st.m[j] = mn;
         st.l[j] *= al;
 #pragma unroll
-        for (int g = 0; g < G; ++g) st.pb[j][g] *= al;
+        for (int g = 0; g < GV; ++g) st.pb[j][g] *= al;
 #pragma unroll
-        for (int h = 0; h < NP; ++h)
+        for (int h = 0; h < NPV; ++h)
 #pragma unroll
           for (int d = 0; d < VDPL; ++d) st.o[j][h][d] *= al;
       }
@@ -519,9 +522,9 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
       st.l[j] += p;
       if constexpr (AFF) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          ws.wrow(lane, g)[j] = p * plane_val<G>(sc.vs, g);
-          st.pb[j][g] = fmaf(p, plane_val<G>(sc.vb, g), st.pb[j][g]);
+        for (int g = 0; g < GV; ++g) {
+          ws.wrow(lane, g)[j] = p * plane_val<GV>(sc.vs, g);
+          st.pb[j][g] = fmaf(p, plane_val<GV>(sc.vb, g), st.pb[j][g]);
         }
       } else {
         ws.wrow(lane, 0)[j] = p;
@@ -530,16 +533,16 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
     wave_lds_sync();
 
     // ---- V phase: o[j][d] += w[row][group][j] * value[row][d], one part of the row at a time
-    RowPart<KCP> vpart;
+    RowPart<KCPV> vpart;
 #pragma unroll
-    for (int h = 0; h < NP; ++h) {
-      RowPart<KCP> vnext;
-      if (h + 1 < NP) vnext = load_row_part<KCP>(vplane, row, ROWB, (h + 1) * KPB);
+    for (int h = 0; h < NPV; ++h) {
+      RowPart<KCPV> vnext;
+      if (h + 1 < NPV) vnext = load_row_part<KCPV>(vplane, row, ROWBV, (h + 1) * KPBV);
       if (h > 0) {
         stage_v(vpart);
         wave_lds_sync();
       }
-      const int vgrp = AFF ? (h * Gm::DPP_ + vsl * VDPL) / Gm::GSZ : 0;
+      const int vgrp = AFF ? (h * Gv::DPP_ + vsl * VDPL) / Gv::GSZ : 0;
 #pragma unroll
       for (int i = 0; i < NBV; ++i) {
         const int r = vrg + VRPL * i;
@@ -555,7 +558,7 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
           for (int j = 0; j < QVW; ++j) wv[j] = ws.wrow(r, vgrp)[j];
         }
         float vv[VDPL];
-        if constexpr (Gm::STR) {
+        if constexpr (Gv::STR) {
           const int ob = vsl * VW;                                // the lane's first byte
           const uint32_t* src = reinterpret_cast<const uint32_t*>(&ws.v[r][ob & ~3]);
           value8_str<BITS>(src[0], src[1], 8u * (uint32_t)(ob & 3), vv);
@@ -575,7 +578,7 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
           for (int d = 0; d < VDPL; ++d) st.o[j][h][d] = fmaf(wv[j], vv[d], st.o[j][h][d]);
       }
       wave_lds_sync();                                            // ws.v is rewritten next
-      if (h + 1 < NP) vpart = vnext;
+      if (h + 1 < NPV) vpart = vnext;
     }
 
     if (!has_next) break;
@@ -589,9 +592,9 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
 // Sum the lanes' shares and write one partial (o, m, l) of QVW vectors: o to orow(j) + dim,
 // (m, l) through set_ml(j, m, l) on lane 0.  m is reported as -inf when no token of the range
 // was visible to a vector.
-template <int BITS, int D, int QVW, int GS, class ORow, class SetML>
-__device__ __forceinline__ void acc_write(Acc<BITS, D, QVW, GS>& st, int lane, ORow orow, SetML set_ml) {
-  using Gm = Geo<BITS, D, GS>;
+template <int BITS, int DV, int QVW, int GS, class ORow, class SetML>
+__device__ __forceinline__ void acc_write(Acc<BITS, DV, QVW, GS>& st, int lane, ORow orow, SetML set_ml) {
+  using Gm = Geo<BITS, DV, GS>;
   constexpr int VDPL = Gm::VDPL, VLPR = Gm::VLPR, G = Gm::G, NP = Gm::NP;
   const int vsl = lane % VLPR, vrg = lane / VLPR;
 #pragma unroll
@@ -691,14 +694,14 @@ __global__ void __launch_bounds__(256) step_prep_kernel(AppendArgs ap, PartialAr
 
 // ------------------------------------------------------------------- fixed partitions
 
-template <int BITS, int D, int QVW, int GS>
+template <int BITS, int D, int DV, int QVW, int GS>
 __global__ void __launch_bounds__(PV_WAVES * 64, 2)
 partial_part_kernel(PartialArgs a) {
   // the waves' tile scratch, then (after a barrier) their partials for the combine
   __shared__ __align__(16) union {
-    WaveScratch<BITS, D, QVW, GS> ws[PV_WAVES];
+    WaveScratch<BITS, DV, QVW, GS> ws[PV_WAVES];
     struct {
-      float o[PV_WAVES][QVW][D];
+      float o[PV_WAVES][QVW][DV];
       float m[PV_WAVES][QVW], l[PV_WAVES][QVW];
     } comb;
   } sh;
@@ -715,21 +718,21 @@ partial_part_kernel(PartialArgs a) {
   if (t0 >= un.len) return;                                      // uniform over the workgroup
   const int t1 = min(un.len, t0 + a.part_tokens);
 
-  Acc<BITS, D, QVW, GS> st;
+  Acc<BITS, DV, QVW, GS> st;
   acc_init(st);
   int cur = t0 + wave * PV_TILE;
-  run_tiles<BITS, D, QVW, GS>(
+  run_tiles<BITS, D, DV, QVW, GS>(
       a, un, t1, [&]() { const int t = cur; cur += PV_WAVES * PV_TILE; return t; }, sh.ws[wave], st, lane);
   __syncthreads();
-  acc_write<BITS, D, QVW, GS>(
+  acc_write<BITS, DV, QVW, GS>(
       st, lane, [&](int j) { return &sh.comb.o[wave][j][0]; },
       [&](int j, float m, float l) { sh.comb.m[wave][j] = m; sh.comb.l[wave][j] = l; });
   __syncthreads();
 
   // combine the waves (log-sum-exp), write this partition's partial
   const int REP = a.HQ / a.HK, N = a.N;
-  for (int e = tid; e < QVW * D; e += PV_WAVES * 64) {
-    const int j = e / D, d = e - j * D;
+  for (int e = tid; e < QVW * DV; e += PV_WAVES * 64) {
+    const int j = e / DV, d = e - j * DV;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < PV_WAVES; ++w) M = fmaxf(M, sh.comb.m[w][j]);
@@ -747,7 +750,7 @@ partial_part_kernel(PartialArgs a) {
     const int jj = un.qg * QVW + j;
     const int h = un.hk * REP + jj / N, i = jj - (jj / N) * N;
     const int64_t idx = (((int64_t)un.b * a.HQ + h) * N + i) * a.num_parts + p;
-    a.opart[idx * D + d] = num;
+    a.opart[idx * DV + d] = num;
     if (d == 0) { a.ml[idx * 2] = M; a.ml[idx * 2 + 1] = den; }
   }
 }
@@ -763,11 +766,11 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
   return x;
 }
 
-template <int BITS, int D, int QVW, int GS>
+template <int BITS, int D, int DV, int QVW, int GS>
 __global__ void __launch_bounds__(VALU_STREAM_WAVES * 64, 1)
 partial_stream_kernel(PartialArgs a) {
   constexpr int NW = VALU_STREAM_WAVES;
-  __shared__ __align__(16) WaveScratch<BITS, D, QVW, GS> ws[NW];
+  __shared__ __align__(16) WaveScratch<BITS, DV, QVW, GS> ws[NW];
   __shared__ int tile_ctr;                                       // next tile of the range
 
   const int lane = threadIdx.x & 63;
@@ -838,10 +841,10 @@ partial_stream_kernel(PartialArgs a) {
     Unit un;
     un.b = b; un.hk = uu / a.qgroups; un.qg = uu - un.hk * a.qgroups; un.len = len;
     un.u = (int64_t)b * HQG + uu;
-    Acc<BITS, D, QVW, GS> st;
+    Acc<BITS, DV, QVW, GS> st;
     acc_init(st);
     const int t0u = t_lo, kb = kbase;
-    run_tiles<BITS, D, QVW, GS>(
+    run_tiles<BITS, D, DV, QVW, GS>(
         a, un, t_end,
         [&]() {
           const int k = uni(kq);
@@ -852,8 +855,8 @@ partial_stream_kernel(PartialArgs a) {
         ws[wave], st, lane);
     kq = uni(kq);
     const int64_t slot = (un.u + g) * NW + wave;
-    acc_write<BITS, D, QVW, GS>(
-        st, lane, [&](int j) { return opart + (slot * QVW + j) * D; },
+    acc_write<BITS, DV, QVW, GS>(
+        st, lane, [&](int j) { return opart + (slot * QVW + j) * DV; },
         [&](int j, float m, float l) { ml[(slot * QVW + j) * 2] = m; ml[(slot * QVW + j) * 2 + 1] = l; });
     kbase += ntiles;
     x += seg;
@@ -872,15 +875,15 @@ partial_stream_kernel(PartialArgs a) {
 
 // ------------------------------------------------------------------- launch
 
-template <int BITS, int D, int QVW, int GS>
+template <int BITS, int D, int DV, int QVW, int GS>
 static hipError_t launch_valu(const PartialArgs& a, int B, bool q_ready, hipStream_t s) {
   const unsigned units = (unsigned)((int64_t)B * a.HK * a.qgroups);
   if (!q_ready) hipLaunchKernelGGL((qprep_kernel<BITS, D, QVW, GS>), dim3(units), dim3(256), 0, s, a);
   if (a.part_tokens > 0) {
     dim3 grid((unsigned)a.num_parts, (unsigned)(a.HK * a.qgroups), (unsigned)B);
-    hipLaunchKernelGGL((partial_part_kernel<BITS, D, QVW, GS>), grid, dim3(PV_WAVES * 64), 0, s, a);
+    hipLaunchKernelGGL((partial_part_kernel<BITS, D, DV, QVW, GS>), grid, dim3(PV_WAVES * 64), 0, s, a);
   } else {
-    hipLaunchKernelGGL((partial_stream_kernel<BITS, D, QVW, GS>), dim3((unsigned)a.num_ranges),
+    hipLaunchKernelGGL((partial_stream_kernel<BITS, D, DV, QVW, GS>), dim3((unsigned)a.num_ranges),
                        dim3(VALU_STREAM_WAVES * 64), 0, s, a);
   }
   return hipGetLastError();
@@ -888,7 +891,8 @@ static hipError_t launch_valu(const PartialArgs& a, int B, bool q_ready, hipStre
 
 template <int BITS, int D, int QVW, int GS>
 static hipError_t launch_step(const AppendArgs& ap, const PartialArgs& a, bool vq, int B, hipStream_t s) {
-  const int64_t total = (int64_t)ap.T * ap.HK * (ap.D / append_ept(BITS));
+  // (the V head dim enters only through ap.Dv)
+  const int64_t total = (int64_t)ap.T * ap.HK * (max(ap.D, ap.Dv) / append_ept(BITS));
   const int na = (int)((total + 255) / 256);
   const int nq = vq ? (int)((int64_t)B * a.HK * a.qgroups) : 0;
   if (na + nq == 0) return hipSuccess;
@@ -900,15 +904,15 @@ static hipError_t launch_step(const AppendArgs& ap, const PartialArgs& a, bool v
   return hipGetLastError();
 }
 
-// one call of F<BITS, D, QVW, GS> for the runtime (D, gs, qvw), or hipErrorInvalidValue
-template <int BITS, int D, int GS, class F>
+// one call of F<BITS, D, DV, QVW, GS> for the runtime qvw, or hipErrorInvalidValue
+template <int BITS, int D, int DV, int GS, class F>
 static hipError_t with_qvw(int qvw, F f) {
   switch (qvw) {
-    case 1: return f.template run<BITS, D, 1, GS>();
-    case 2: return f.template run<BITS, D, 2, GS>();
-    case 4: return f.template run<BITS, D, 4, GS>();
+    case 1: return f.template run<BITS, D, DV, 1, GS>();
+    case 2: return f.template run<BITS, D, DV, 2, GS>();
+    case 4: return f.template run<BITS, D, DV, 4, GS>();
     case 8:
-      if constexpr (valu_max_qvw(BITS, D, GS) >= 8) return f.template run<BITS, D, 8, GS>();
+      if constexpr (valu_max_qvw(BITS, D, DV, GS) >= 8) return f.template run<BITS, D, DV, 8, GS>();
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -917,53 +921,70 @@ static hipError_t with_qvw(int qvw, F f) {
 template <int BITS, int D, class F>
 static hipError_t with_group(int gs, int qvw, F f) {
   if constexpr (BITS == 16) {
-    return with_qvw<BITS, D, 64>(qvw, f);                    // bf16 pages have no scale groups
+    return with_qvw<BITS, D, D, 64>(qvw, f);                 // bf16 pages have no scale groups
   } else {
     switch (gs) {
-      case 32: return with_qvw<BITS, D, 32>(qvw, f);
-      case 64: return with_qvw<BITS, D, 64>(qvw, f);
+      case 32: return with_qvw<BITS, D, D, 32>(qvw, f);
+      case 64: return with_qvw<BITS, D, D, 64>(qvw, f);
       case 128:
-        if constexpr (D >= 128) return with_qvw<BITS, D, 128>(qvw, f);
+        if constexpr (D >= 128) return with_qvw<BITS, D, D, 128>(qvw, f);
         return hipErrorInvalidValue;
       default: return hipErrorInvalidValue;
     }
   }
 }
 
+// V rows of a head dim of their own: DV = D / 2 or 2 D, 64-element scale groups (bf16 pages
+// have none), bf16, 8-, 4- and 2-bit pages (valu_dv_ok)
+template <int BITS, int D, class F>
+static hipError_t with_dv(int DV, int gs, int qvw, F f) {
+  if constexpr (BITS == 16 || BITS == 8 || BITS == 4 || BITS == 2) {
+    if (BITS != 16 && gs != 64) return hipErrorInvalidValue;
+    if constexpr (D >= 128) {
+      if (2 * DV == D) return with_qvw<BITS, D, D / 2, 64>(qvw, f);
+    }
+    if constexpr (D <= 128) {
+      if (DV == 2 * D) return with_qvw<BITS, D, 2 * D, 64>(qvw, f);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int BITS, class F>
-static hipError_t with_shape(int D, int gs, int qvw, F f) {
+static hipError_t with_shape(int D, int DV, int gs, int qvw, F f) {
   switch (D) {
     case 64:
-      if constexpr (valu_row_ok(BITS, 64)) return with_group<BITS, 64>(gs, qvw, f);
+      if constexpr (valu_row_ok(BITS, 64)) return DV == D ? with_group<BITS, 64>(gs, qvw, f) : with_dv<BITS, 64>(DV, gs, qvw, f);
       return hipErrorInvalidValue;
-    case 128: return with_group<BITS, 128>(gs, qvw, f);
-    case 256: return with_group<BITS, 256>(gs, qvw, f);
+    case 128: return DV == D ? with_group<BITS, 128>(gs, qvw, f) : with_dv<BITS, 128>(DV, gs, qvw, f);
+    case 256: return DV == D ? with_group<BITS, 256>(gs, qvw, f) : with_dv<BITS, 256>(DV, gs, qvw, f);
     default: return hipErrorInvalidValue;
   }
 }
 
 struct PartialLaunch {
   const PartialArgs& a; int B; bool q_ready; hipStream_t s;
-  template <int BITS, int D, int QVW, int GS>
-  hipError_t run() const { return launch_valu<BITS, D, QVW, GS>(a, B, q_ready, s); }
+  template <int BITS, int D, int DV, int QVW, int GS>
+  hipError_t run() const { return launch_valu<BITS, D, DV, QVW, GS>(a, B, q_ready, s); }
 };
 
 struct StepLaunch {
   const AppendArgs& ap; const PartialArgs& a; bool vq; int B; hipStream_t s;
-  template <int BITS, int D, int QVW, int GS>
+  template <int BITS, int D, int DV, int QVW, int GS>
   hipError_t run() const { return launch_step<BITS, D, QVW, GS>(ap, a, vq, B, s); }
 };
 
 template <int BITS>
-hipError_t launch_valu_bits(const PartialArgs& a, int D, int gs, int qvw, int B, bool q_ready, hipStream_t s) {
-  return with_shape<BITS>(D, gs, qvw, PartialLaunch{a, B, q_ready, s});
+hipError_t launch_valu_bits(const PartialArgs& a, int D, int DV, int gs, int qvw, int B, bool q_ready, hipStream_t s) {
+  return with_shape<BITS>(D, DV, gs, qvw, PartialLaunch{a, B, q_ready, s});
 }
 
 template <int BITS>
 hipError_t launch_step_bits(const AppendArgs& ap, const PartialArgs& a, int D, int gs, int qvw, bool vq, int B,
                             hipStream_t s) {
-  // without the q copy the step kernel is only the append: one instance per (D, group)
-  return with_shape<BITS>(D, gs, vq ? qvw : 1, StepLaunch{ap, a, vq, B, s});
+  // without the q copy the step kernel is only the append: one instance per (D, group); it reads
+  // the V head dim from ap, so every V head dim shares the K head dim's instance
+  return with_shape<BITS>(D, D, gs, vq ? qvw : 1, StepLaunch{ap, a, vq, B, s});
 }
 
 }  // namespace kvq

@@ -51,7 +51,8 @@ typedef enum kvq_status {
 /* Pool planes, each shaped [num_blocks, num_kv_heads, block_size, width] ([P134]
  * cache.ts, class BlockPool).  bf16 pages (bits == 16) have only K and V (uint16, width
  * head_dim).  Affine pages have packed codes K and V (uint32, width head_dim*bits/32) and
- * bf16 scale and bias planes of width head_dim/group_size.  A row's codes are one
+ * bf16 scale and bias planes of width head_dim/group_size.  The V planes take v_head_dim in
+ * place of head_dim (the pool's vHeadDim, which defaults to headDim).  A row's codes are one
  * little-endian bit stream: element i in stream bits [bits*i, bits*i + bits), stream bit k in
  * bit k%32 of word k/32.  For widths dividing 32 that is bits [bits*(i%P), bits*(i%P+1)) of
  * word i/P, P = 32/bits ([P50] paged.ts, paged_attention_affine_partial); 3-, 5- and 6-bit
@@ -75,6 +76,10 @@ typedef struct kvq_pool_desc {
   int32_t bits;          /* 16 = bf16 pages; 8, 6, 5, 4, 3 or 2 = affine codes; a row of codes
                             (head_dim*bits/8 bytes) must be whole 16-byte chunks */
   int32_t group_size;    /* elements per scale/bias group along the head dim: 32, 64 or 128 */
+  int32_t v_head_dim;    /* DV, the V rows' head dim ([P50] paged.ts reads DK and DV); 0 = head_dim.
+                            A DV other than head_dim is read by the vector engine for bf16, 8-,
+                            4- and 2-bit pages with group_size 64 (affine) and DV = head_dim / 2
+                            or 2 * head_dim within 64..256; other pairs are KVQ_ERR_UNSUPPORTED */
 } kvq_pool_desc;
 
 typedef struct kvq_pool kvq_pool;  /* opaque */
@@ -111,7 +116,7 @@ int kv_pool_describe(const kvq_pool* pool, kvq_pool_desc* out);
  * group_size elements):  mn, mx = min, max; scale = (mx - mn) / (2^bits - 1) in f32,
  * rounded up to bf16; bias = mn; code = clamp(rint((x - bias) / scale), 0, 2^bits - 1)
  * (round half to even; a group with scale 0 stores code 0); codes packed low-first.
- *   k, v   device bf16 [T, num_kv_heads, head_dim]
+ *   k, v   device bf16 [T, num_kv_heads, head_dim] and [T, num_kv_heads, v_head_dim]
  *   slots  device int64 [T]: physical slot = block * block_size + row; a negative slot
  *          skips its row; a slot >= num_blocks * block_size is skipped as well.
  * Rows of one call must target distinct slots.  T == 0 is a no-op. */
@@ -149,7 +154,7 @@ typedef struct kvq_decode_shape {
  *   KVQ_ENGINE_VECTOR: vector ALU -- v_dot2_f32_bf16 for q.k, f32 FMA for P.V; every format.
  *   KVQ_ENGINE_MATRIX: matrix cores -- q.k with exact bf16 products, P.V with exact f16 codes
  *     against the weight split into two f16 halves (~2^-22 relative); 4-bit pages, head_dim
- *     128 or 256, the balanced stream only (partition_tokens <= 0).  It serves the GQA groups where the vector ALU
+ *     128 or 256 (v_head_dim the same), the balanced stream only (partition_tokens <= 0).  It serves the GQA groups where the vector ALU
  *     rather than HBM bounds the pass ([P50] multi-query.ts puts a KV head's query rows on the
  *     matrix unit for the same reason).
  *   KVQ_ENGINE_AUTO: the vector engine. */
@@ -166,6 +171,7 @@ int32_t paged_decode_partition_tokens(const kvq_pool* pool, const kvq_decode_sha
 /* Decode attention for N <= KVQ_MAX_Q_ROWS query rows per sequence read straight from the pages
  * ([P50] paged.ts pagedAttentionView.attend, direct route; kvq4-decode.ts):
  *   out[b, h, i, :] = sum_t softmax_t(scale * q[b,h,i,:] . K[b,t,g,:]) V[b,t,g,:]
+ * (K rows of head_dim, V rows and out rows of v_head_dim)
  * over t < lengths[b] - N + i + 1, with g = h / (HQ / HK) (GQA), K and V the dequantized
  * page rows (scale * code + bias in f32) or the bf16 rows.  Token t of sequence b sits in
  * block block_table[b, t / BS], row t % BS.  Computed as a split-K partial pass (online
@@ -176,7 +182,7 @@ int32_t paged_decode_partition_tokens(const kvq_pool* pool, const kvq_decode_sha
  *   lengths      device int32 [B]; each in [N, max_len] (tokens cached, counting the N
  *                new rows); not checked on the device
  *   workspace    device, >= paged_decode_workspace_bytes(pool, shape) bytes
- *   out          device [B, HQ, N, head_dim], bf16 (round to nearest even) or f32
+ *   out          device [B, HQ, N, v_head_dim], bf16 (round to nearest even) or f32
  * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED (N > KVQ_MAX_Q_ROWS, HQ % HK != 0),
  * KVQ_ERR_WORKSPACE. */
 int paged_decode_attention(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table,
@@ -202,7 +208,8 @@ int paged_decode_merge(const kvq_pool* pool, const int32_t* lengths, const kvq_d
  * lengths[b] - N + i, block block_table[b, pos / BS], row pos % BS -- and then
  * paged_decode_attention runs over the updated pool, all on the given stream with no host-side
  * slot mapping.
- *   k_new, v_new  device bf16 [B, N, num_kv_heads, head_dim], 16-byte aligned
+ *   k_new, v_new  device bf16 [B, N, num_kv_heads, head_dim] and [B, N, num_kv_heads, v_head_dim],
+ *                 16-byte aligned
  *   other arguments as paged_decode_attention; lengths count the new rows, and the blocks of
  *   the new positions must already be in the table (allocation is the caller's).
  * A new row whose position is outside [0, min(max_len, max_blocks_per_seq * BS)) or whose

@@ -25,7 +25,7 @@ def i64_dev(a: np.ndarray) -> torch.Tensor:
 
 
 def new_pool(w, num_blocks=None) -> kvq.Pool:
-    return kvq.Pool(num_blocks or w.num_blocks, w.HK, w.BS, w.D, w.bits, w.group)
+    return kvq.Pool(num_blocks or w.num_blocks, w.HK, w.BS, w.D, w.bits, w.group, v_head_dim=w.DV)
 
 
 def fill_pool(w, pool: kvq.Pool, seqs=None) -> None:

@@ -60,7 +60,7 @@ def test_probe_read_rejects_bad_arguments(lib):
 
 
 def test_struct_layouts():
-    assert ctypes.sizeof(kvq.PoolDesc) == 24
+    assert ctypes.sizeof(kvq.PoolDesc) == 28
     assert ctypes.sizeof(kvq.DecodeShape) == 32
 
 
@@ -123,6 +123,57 @@ def test_straddling_widths(lib, bits, D, ok):
         with pytest.raises(kvq.KvqError) as e:
             kvq.kv_pool_wrap(d, [16] * 6)
         assert e.value.code == -2
+
+
+@pytest.mark.parametrize("bits,D,DV,group,ok", [
+    (16, 128, 64, 64, True), (16, 128, 256, 64, True), (16, 256, 128, 64, True), (16, 64, 128, 64, True),
+    (8, 256, 128, 64, True), (4, 128, 64, 64, True), (4, 64, 128, 64, True), (2, 128, 256, 64, True),
+    (4, 256, 64, 64, False),        # a quarter: not read
+    (4, 128, 64, 32, False),        # group 32 with a V head dim of its own
+    (5, 256, 128, 32, False),       # straddling width
+    (16, 128, 512, 64, False), (16, 128, 96, 64, False)])
+def test_value_head_dim(lib, bits, D, DV, group, ok):
+    """A V head dim of its own (the pages' vHeadDim): the V planes take DV in place of D; 0 stands
+    for D and the pool reports DV explicitly."""
+    d = kvq.PoolDesc(4, 2, 16, D, bits, group, DV)
+    rows = 4 * 2 * 16
+    if not ok:
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kv_pool_wrap(d, [16] * 6)
+        assert e.value.code == -2
+        return
+    h = kvq.kv_pool_wrap(d, [16] * 6)
+    if bits == 16:
+        assert kvq.kv_pool_plane_bytes(d, 0) == rows * D * 2
+        assert kvq.kv_pool_plane_bytes(d, 1) == rows * DV * 2
+    else:
+        assert kvq.kv_pool_plane_bytes(d, 0) == rows * D * bits // 8
+        assert kvq.kv_pool_plane_bytes(d, 1) == rows * DV * bits // 8
+        assert kvq.kv_pool_plane_bytes(d, 2) == rows * (D // group) * 2
+        assert kvq.kv_pool_plane_bytes(d, 4) == rows * (DV // group) * 2
+        assert kvq.kv_pool_plane_bytes(d, 5) == rows * (DV // group) * 2
+    out = kvq.PoolDesc()
+    assert lib.kv_pool_describe(h, ctypes.byref(out)) == 0 and out.v_head_dim == DV
+    kvq.kv_pool_destroy(h)
+    # a decode shape over such a pool has a workspace; the matrix engine reads DV == D only
+    h = kvq.kv_pool_wrap(d, [256] * 6)
+    s = kvq.DecodeShape(2, 8, 1, 64, 1024, 0, 0, 1)
+    assert lib.paged_decode_workspace_bytes(h, ctypes.byref(s)) > 0
+    s.engine = 2
+    assert lib.paged_decode_workspace_bytes(h, ctypes.byref(s)) == 0
+    kvq.kv_pool_destroy(h)
+
+
+def test_value_head_dim_zero_means_head_dim(lib):
+    d = kvq.PoolDesc(4, 2, 16, 128, 4, 64)                  # v_head_dim left 0
+    h = kvq.kv_pool_wrap(d, [16] * 6)
+    out = kvq.PoolDesc()
+    assert lib.kv_pool_describe(h, ctypes.byref(out)) == 0 and out.v_head_dim == 128
+    kvq.kv_pool_destroy(h)
+    d.v_head_dim = -64
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kv_pool_wrap(d, [16] * 6)
+    assert e.value.code == -1
 
 
 class _FakePool:
