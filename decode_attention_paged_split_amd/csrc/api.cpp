@@ -454,7 +454,22 @@ struct Plan {
   kvq::MergeArgs m;
   int qvw;
   bool mfma;
+  int merge_threads;
 };
+
+// Merge workgroup size: one output row per workgroup, D/4 threads per stream of partials, 64 to
+// 256 threads.  Few rows (under 8 per compute unit) leave the merge latency-bound: streams of about
+// four partials each; many rows keep every compute unit busy anyway, and then streams of about
+// eight partials waste fewer waves on the row's set-up (measured: 512 rows of 17-40 partials run
+// fastest at 4-10 per stream, 8192 rows of 3-10 partials at one stream).  Partials per row: the
+// fixed partitions' count, or the stream slots of a unit spread over its rows.
+int merge_threads_for(int dv, int pt, int parts, const StreamGeom& sg, double units, double rows) {
+  const double per_row = pt > 0 ? (double)parts : (double)sg.sub * (sg.ranges + units) / units;
+  const double per_stream = rows >= 8.0 * device_cus() ? 8.0 : 4.0;
+  int streams = 1;
+  while (streams * 2 <= per_row / per_stream) streams *= 2;
+  return std::max(64, std::min(256, (dv / 4) * streams));
+}
 
 hipError_t launch_plan_partial(const Plan& P, const kvq_pool* pool, int B, hipStream_t st, bool q_ready = false) {
   return timed(KVQ_TIMING_PARTIAL, st, [&] {
@@ -465,7 +480,7 @@ hipError_t launch_plan_partial(const Plan& P, const kvq_pool* pool, int B, hipSt
 }
 
 hipError_t launch_plan_merge(const Plan& P, int B, hipStream_t st) {
-  return timed(KVQ_TIMING_MERGE, st, [&] { return kvq::launch_merge(P.m, B, st); });
+  return timed(KVQ_TIMING_MERGE, st, [&] { return kvq::launch_merge(P.m, B, P.merge_threads, st); });
 }
 
 int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, const int32_t* lengths, float scale,
@@ -510,6 +525,9 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   const StreamGeom sg = stream_geom(pool, shape);
   a.batch = shape->batch; a.num_ranges = sg.ranges; a.range_sub = sg.sub; a.min_tokens = sg.min_tokens;
 
+  P->merge_threads = merge_threads_for(d.v_head_dim, pt, parts, sg,
+                                       (double)shape->batch * d.num_kv_heads * a.qgroups,
+                                       (double)shape->batch * shape->num_q_heads * shape->q_rows);
   kvq::MergeArgs& m = P->m;
   m = kvq::MergeArgs{};
   m.opart = a.opart; m.ml = a.ml; m.lengths = lengths; m.out = out;

@@ -84,7 +84,8 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 // scale-group size (affine pages); D, DV: the K and V head dims
 hipError_t launch_partial(const PartialArgs& a, int bits, int D, int DV, int gs, int qvw, int B, bool q_ready,
                           hipStream_t stream);
-hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t stream);
+// threads: 64, 128 or 256 per output row (at least D / 4)
+hipError_t launch_merge(const MergeArgs& a, int B, int threads, hipStream_t stream);
 // decode step: the new rows' append (slots from the block table) and, for the vector engine, the
 // q copy, in one launch
 hipError_t launch_step_prep(const AppendArgs& ap, const PartialArgs& a, int bits, int D, int DV, int gs, int qvw,

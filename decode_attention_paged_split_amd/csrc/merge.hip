@@ -6,9 +6,11 @@
 // M = max_p m_p; partitions whose max is -inf (no visible token) are skipped.  Maxima are in
 // log2 units here (the partial kernel scales scores by log2(e)), so the weights are exp2.
 // One workgroup per output row, one pass over the partials: thread (stream s, dim lane dl) owns
-// head dims 4 dl .. 4 dl + 3 and partials s, s + S, ...; it loads each partial's (m, l) and o
-// together and folds them into a running (max, sum of weights, weighted o) (the weights are
-// rescaled when the max moves), and the S streams' states are combined in LDS the same way.
+// head dims 4 dl .. 4 dl + 3 and partials s, s + S, ... (S = threads / (D / 4); the host sizes
+// the workgroup, 64 to 256 threads, for about five partials per stream); it loads each
+// partial's (m, l) and o together and folds them into a running (max, sum of weights, weighted
+// o) (the weights are rescaled when the max moves), and the S streams' states are combined in
+// LDS the same way.
 // Output is bf16 (round to nearest even) or f32.
 // Stream schedule: the stream of T tokens is cut into R = min(num_ranges, ceil(T / min_tokens))
 // ranges; a unit's partials sit in range_sub consecutive slots per range it meets, from slot
@@ -22,7 +24,8 @@ namespace kvq {
 
 // ------------------------------------------------------------------------------ merge
 
-__global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
+template <int NT>
+__global__ void __launch_bounds__(NT) merge_kernel(MergeArgs a) {
   extern __shared__ float sw[];                 // the streams' partial states
   const int row = blockIdx.x;                   // (b, h, i)
   const int b = row / (a.HQ * a.N);
@@ -127,12 +130,22 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   }
 }
 
-hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t s) {
-  const unsigned rows = (unsigned)(B * a.HQ * a.N);
-  // the 256 threads' float4 sums and each stream's (max, weight sum)
-  const size_t shm = (size_t)(256 * 4 + 2 * 256) * sizeof(float);
-  hipLaunchKernelGGL(merge_kernel, dim3(rows), dim3(256), shm, s, a);
+template <int NT>
+static hipError_t launch_merge_nt(const MergeArgs& a, unsigned rows, hipStream_t s) {
+  // the threads' float4 sums and each stream's (max, weight sum)
+  const size_t shm = (size_t)(NT * 4 + 2 * NT) * sizeof(float);
+  hipLaunchKernelGGL(merge_kernel<NT>, dim3(rows), dim3(NT), shm, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, int B, int threads, hipStream_t s) {
+  const unsigned rows = (unsigned)(B * a.HQ * a.N);
+  switch (threads) {
+    case 64: return launch_merge_nt<64>(a, rows, s);
+    case 128: return launch_merge_nt<128>(a, rows, s);
+    case 256: return launch_merge_nt<256>(a, rows, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace kvq
