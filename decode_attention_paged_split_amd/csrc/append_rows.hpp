@@ -67,20 +67,29 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int64_t gid) {
   const int off = store ? (int)(slot % a.BS) : 0;
   const int64_t prow = (phys * a.HK + head) * a.BS + off;   // row index within a plane
 
+  // the K and V chunks are loaded before anything is stored (the stores may alias the sources
+  // as far as the compiler knows, so loads after a store would wait for it); a row's width is D
+  // for K and Dv for V, and chunks beyond it (the narrower row's) are whole scale groups that
+  // load and store nothing
+  uint32_t src_w[2][EPT / 2];
+#pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
-    // this pass's row width; chunks beyond it (the narrower of K and V) are whole scale groups
-    // that load and store nothing
     const int dk = kv ? a.Dv : a.D;
     const bool on = live && chunk * EPT < dk;
-    const bool put = store && on;
-    const uint16_t* src = kv ? a.v : a.k;
-    const uint4* s4 = reinterpret_cast<const uint4*>(src + row * dk + chunk * EPT);
-    uint32_t w[EPT / 2];
+    const uint4* s4 = reinterpret_cast<const uint4*>((kv ? a.v : a.k) + row * dk + chunk * EPT);
 #pragma unroll
     for (int q = 0; q < EPT / 8; ++q) {
       const uint4 x = on ? s4[q] : make_uint4(0, 0, 0, 0);
-      w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
+      src_w[kv][4 * q] = x.x; src_w[kv][4 * q + 1] = x.y; src_w[kv][4 * q + 2] = x.z; src_w[kv][4 * q + 3] = x.w;
     }
+  }
+
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    const int dk = kv ? a.Dv : a.D;
+    const bool on = live && chunk * EPT < dk;
+    const bool put = store && on;
+    const uint32_t* w = src_w[kv];
     if constexpr (BITS == 16) {
       if (put) {
         uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(kv ? a.v_plane : a.k_plane) +

@@ -265,7 +265,7 @@ __global__ void __launch_bounds__(MF_WAVES * 64, 1)
 partial_mfma_kernel(PartialArgs a) {
   const KUnpack ku = k_unpack_consts();
   using Mg = MGeo<D>;
-  constexpr int G = Mg::G, KSTEPS = Mg::KSTEPS, KSETS = Mg::KSETS, DT = Mg::DT, ROWB = Mg::ROWB;
+  constexpr int G = Mg::G, KSTEPS = Mg::KSTEPS, KSETS = Mg::KSETS, DT = Mg::DT;
   constexpr int CPR = Mg::CPR, NVL = Mg::NVL;
   __shared__ __align__(16) MScratch<D> scr[MF_WAVES];
 

@@ -635,15 +635,24 @@ __device__ __forceinline__ int clamp_len(const PartialArgs& a, int b) {
 
 // ------------------------------------------------------------------- q in the codes' pair order
 
-// One workgroup (256 threads) per unit.  Block b = ((g * NHB + hb) * QVW + j) of Q_BLOCK_WORDS
-// words holds the 16 q pairs of 16-pair block hb of scale group g for vector j, in the order the
-// K phase meets the codes; the last block of each group then holds (affine pages) the f32 sum of
-// q over the group's dims, the bias term's factor (one wave per (group, vector), each lane adding
-// GSZ / 64 dims).
+// One workgroup (PREP_THREADS threads) per unit.  Block b = ((g * NHB + hb) * QVW + j) of
+// Q_BLOCK_WORDS words holds the 16 q pairs of 16-pair block hb of scale group g for vector j, in
+// the order the K phase meets the codes; the last block of each group then holds (affine pages)
+// the f32 sum of q over the group's dims, the bias term's factor (one wave per (group, vector),
+// each lane adding GSZ / 64 dims).  Every load is issued before the first store (the stores may
+// alias q as far as the compiler knows, so a load after a store would wait for it): the kernel
+// takes about one memory round trip instead of one per element.
+constexpr int PREP_THREADS = 256;
+
 template <int BITS, int D, int QVW, int GS>
 __device__ __forceinline__ void prep_q(const PartialArgs& a, int64_t u) {
   using Gm = Geo<BITS, D, GS>;
   constexpr int G = Gm::G, NHB = Gm::NHB, GSZ = Gm::GSZ, QBS = Q_BLOCK_WORDS;
+  constexpr int NE = G * NHB * QVW * 16;                       // q pairs of the unit
+  constexpr int PER = (NE + PREP_THREADS - 1) / PREP_THREADS;  // pairs per thread
+  constexpr int NW = PREP_THREADS / 64;
+  constexpr int NGJ = G * QVW, PERW = (NGJ + NW - 1) / NW;      // (group, vector) sums per wave
+  constexpr int KS = GSZ / 64 + (GSZ < 64);                     // q elements per lane and sum
   const int qg = (int)(u % a.qgroups);
   const int hk = (int)((u / a.qgroups) % a.HK);
   const int b = (int)(u / ((int64_t)a.qgroups * a.HK));
@@ -652,39 +661,67 @@ __device__ __forceinline__ void prep_q(const PartialArgs& a, int64_t u) {
     const int jj = qg * QVW + j, h = hk * REP + jj / N, i = jj - (jj / N) * N;
     return a.q + (((int64_t)b * a.HQ + h) * N + i) * D;
   };
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t pr[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int e = tid + PREP_THREADS * r;
+    pr[r] = 0;
+    if (e < NE) {
+      const int blk = e / 16, p = e - blk * 16;
+      const int j = blk % QVW, ghb = blk / QVW;                 // ghb = g * NHB + hb
+      int lo, hi;
+      pair_dims<BITS>(ghb * 16 + p, lo, hi);
+      const uint16_t* q = qrow(j);
+      pr[r] = (uint32_t)q[lo] | ((uint32_t)q[hi] << 16);
+    }
+  }
+  float xs[PERW][KS];
+  if constexpr (Gm::AFF) {
+#pragma unroll
+    for (int it = 0; it < PERW; ++it) {
+      const int gj = wave + NW * it;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        xs[it][k] = 0.0f;
+        if (gj < NGJ && k * 64 + lane < GSZ) {
+          const int g = gj / QVW, j = gj - g * QVW;
+          xs[it][k] = bf16_to_f32(qrow(j)[g * GSZ + k * 64 + lane]);
+        }
+      }
+    }
+  }
   uint32_t* out = a.qp + u * (G * NHB * QVW * QBS);
-  for (int e = threadIdx.x; e < G * NHB * QVW * 16; e += blockDim.x) {
-    const int blk = e / 16, p = e - blk * 16;
-    const int j = blk % QVW, ghb = blk / QVW;                     // ghb = g * NHB + hb
-    int lo, hi;
-    pair_dims<BITS>(ghb * 16 + p, lo, hi);
-    const uint16_t* q = qrow(j);
-    out[blk * QBS + p] = (uint32_t)q[lo] | ((uint32_t)q[hi] << 16);
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int e = tid + PREP_THREADS * r;
+    if (e < NE) out[(e / 16) * QBS + (e % 16)] = pr[r];
   }
   if constexpr (Gm::AFF) {
-    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-    for (int gj = threadIdx.x >> 6; gj < G * QVW; gj += nw) {
-      const int g = gj / QVW, j = gj - g * QVW;
-      const uint16_t* q = qrow(j) + g * GSZ;
+#pragma unroll
+    for (int it = 0; it < PERW; ++it) {
+      const int gj = wave + NW * it;
       float x = 0.0f;
 #pragma unroll
-      for (int k = 0; k < GSZ / 64 + (GSZ < 64); ++k)
-        if (k * 64 + lane < GSZ) x += bf16_to_f32(q[k * 64 + lane]);
+      for (int k = 0; k < KS; ++k) x += xs[it][k];
       const float s = block_reduce<OpAdd, 1, 64>(x);
-      if (lane == 0) out[((g * NHB + NHB - 1) * QVW + j) * QBS + 16] = __float_as_uint(s);
+      if (gj < NGJ && lane == 0) {
+        const int g = gj / QVW, j = gj - g * QVW;
+        out[((g * NHB + NHB - 1) * QVW + j) * QBS + 16] = __float_as_uint(s);
+      }
     }
   }
 }
 
 template <int BITS, int D, int QVW, int GS>
-__global__ void __launch_bounds__(256) qprep_kernel(PartialArgs a) {
+__global__ void __launch_bounds__(PREP_THREADS) qprep_kernel(PartialArgs a) {
   prep_q<BITS, D, QVW, GS>(a, blockIdx.x);
 }
 
 // Decode step, first launch: blocks [0, na) append the step's new rows (slots from the block
 // table), blocks [na, na + units) prepare q for the vector engine.
 template <int BITS, int D, int QVW, int GS, bool VQ>
-__global__ void __launch_bounds__(256) step_prep_kernel(AppendArgs ap, PartialArgs a, int na) {
+__global__ void __launch_bounds__(PREP_THREADS) step_prep_kernel(AppendArgs ap, PartialArgs a, int na) {
   if ((int)blockIdx.x < na) {
     append_rows<BITS, Geo<BITS, D, GS>::GSZ>(ap, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
   } else if constexpr (VQ) {
@@ -878,7 +915,7 @@ partial_stream_kernel(PartialArgs a) {
 template <int BITS, int D, int DV, int QVW, int GS>
 static hipError_t launch_valu(const PartialArgs& a, int B, bool q_ready, hipStream_t s) {
   const unsigned units = (unsigned)((int64_t)B * a.HK * a.qgroups);
-  if (!q_ready) hipLaunchKernelGGL((qprep_kernel<BITS, D, QVW, GS>), dim3(units), dim3(256), 0, s, a);
+  if (!q_ready) hipLaunchKernelGGL((qprep_kernel<BITS, D, QVW, GS>), dim3(units), dim3(PREP_THREADS), 0, s, a);
   if (a.part_tokens > 0) {
     dim3 grid((unsigned)a.num_parts, (unsigned)(a.HK * a.qgroups), (unsigned)B);
     hipLaunchKernelGGL((partial_part_kernel<BITS, D, DV, QVW, GS>), grid, dim3(PV_WAVES * 64), 0, s, a);
@@ -893,14 +930,14 @@ template <int BITS, int D, int QVW, int GS>
 static hipError_t launch_step(const AppendArgs& ap, const PartialArgs& a, bool vq, int B, hipStream_t s) {
   // (the V head dim enters only through ap.Dv)
   const int64_t total = (int64_t)ap.T * ap.HK * (max(ap.D, ap.Dv) / append_ept(BITS));
-  const int na = (int)((total + 255) / 256);
+  const int na = (int)((total + PREP_THREADS - 1) / PREP_THREADS);
   const int nq = vq ? (int)((int64_t)B * a.HK * a.qgroups) : 0;
   if (na + nq == 0) return hipSuccess;
   if (vq)
-    hipLaunchKernelGGL((step_prep_kernel<BITS, D, QVW, GS, true>), dim3((unsigned)(na + nq)), dim3(256), 0, s, ap, a,
+    hipLaunchKernelGGL((step_prep_kernel<BITS, D, QVW, GS, true>), dim3((unsigned)(na + nq)), dim3(PREP_THREADS), 0, s, ap, a,
                        na);
   else
-    hipLaunchKernelGGL((step_prep_kernel<BITS, D, QVW, GS, false>), dim3((unsigned)na), dim3(256), 0, s, ap, a, na);
+    hipLaunchKernelGGL((step_prep_kernel<BITS, D, QVW, GS, false>), dim3((unsigned)na), dim3(PREP_THREADS), 0, s, ap, a, na);
   return hipGetLastError();
 }
 
