@@ -1,5 +1,8 @@
 // Split-K partial kernel of paged decode attention (vector ALU engine): the kernels, their
-// launchers by bit width (instantiated once per width in partial_valu_b{16,8,4,2}.hip).
+// launchers by bit width (instantiated once per width in partial_valu_b{16,8,6,5,4,3,2}.hip).
+// Template parameters: BITS (page format), D (K head dim: the K phase, the q copy, K's scale
+// groups), DV (V head dim: the V rows, weights, bias sums, accumulators and partial rows; the
+// pages' vHeadDim), QVW (query vectors per wave), GS (scale-group size).
 //
 // What is computed follows "@mlx-bun/inference 0.0.0-stage -> 1.0.0", diff page 50:
 //  * paged.ts, paged_attention_partial / paged_attention_affine_partial: token t of a
