@@ -48,12 +48,16 @@ def log(*a):
 
 def kernel_source_hash() -> str:
     """Hash of the sources that decide what the partial kernel reads and writes (its code and the
-    host-side launch geometry)."""
+    host-side launch geometry), comments and blank lines left out: a change of wording keeps the
+    counters that were taken on the same code."""
     h = hashlib.sha256()
     for f in ("partial_valu.hip", "partial_valu_impl.hpp", "partial_valu_b4.hip", "device_common.hpp",
               "kernels.hpp", "api.cpp"):
-        with open(os.path.join(ROOT, "decode_attention_paged_split_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "decode_attention_paged_split_amd", "csrc", f), encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
