@@ -102,3 +102,17 @@ def test_matrix_engine_rejects_value_dim():
     with pytest.raises(kvq.KvqError, match="matrix-core"):
         G.run_decode(w, pool, engine=kvq.ENGINE_MATRIX)
     pool.close()
+
+
+@pytest.mark.parametrize("bits,D,DV", [(4, 256, 128), (16, 64, 128)])
+def test_window_value_dim(bits, D, DV):
+    """A window of 12 rows per sequence (more than a decode step's 8) with V rows of their own
+    head dim: every block of query vectors of a KV head is one more unit of the partial pass."""
+    print(f"window bits={bits} D={D} DV={DV}", flush=True)
+    w = make_workload("c3", B=2, len_lo=150, len_hi=400, bits=bits, D=D, DV=DV, HQ=8, HK=2, N=12)
+    ref = attention.workload_output(w)
+    pool = G.new_pool(w)
+    G.fill_pool(w, pool)
+    for pt in (kvq.PARTITION_STREAM, 128):
+        G.check_f32(G.run_decode(w, pool, partition_tokens=pt), ref, tag=f"window DV={DV} pt={pt}")
+    pool.close()
