@@ -23,8 +23,8 @@ Recipe (numpy PCG64; every stream keyed by a SeedSequence):
 
 The five named workloads follow the decode shapes the pages discuss: one-row GQA decode
 over a contiguous 4-bit cache with head dim 256, and paged decode over bf16 or
-affine-quantized pages with a shuffled block table (see the design doc in the repository
-root for the table of shapes).
+affine-quantized pages with a shuffled block table; ``WORKLOADS`` below gives each one's
+shape.
 """
 from __future__ import annotations
 
