@@ -72,15 +72,19 @@ def check_f32(got: np.ndarray, ref: np.ndarray, atol=2e-3, rel_l2=2e-3, tag=""):
 
 
 def check_bf16(got_bits: np.ndarray, ref: np.ndarray, tag=""):
-    """bf16 output vs the oracle rounded to bf16: rel L2 <= 2e-3 and max abs <= max(2e-3, one bf16
-    ulp of the reference value)."""
+    """bf16 output vs the oracle rounded to bf16 (RNE of its f32 value): rel L2 <= 2e-3 and max abs
+    <= max(2e-3, one bf16 ulp of the reference value).  The comparison is with the rounded oracle:
+    the rounding alone moves a small output tensor by up to ~2e-3 in rel L2 (bf16 keeps 8
+    significant bits), so against the unrounded f64 values even the correctly rounded answer
+    could fail the bound."""
     got = bf16_to_f64(got_bits)
     ref32 = ref.astype(np.float32)
+    ref16 = bf16_to_f64(rne_f32_to_bf16(ref32))
     u = ref32.view(np.uint32)
     exp = ((u >> 23) & 0xFF).astype(np.int64) - 127
     ulp = np.ldexp(1.0, np.maximum(exp, -126) - 7)
-    err = np.abs(got - ref)
+    err = np.abs(got - ref16)
     assert np.all(err <= np.maximum(2e-3, ulp)), f"{tag}: bf16 max abs {err.max():.3e}"
-    rl2 = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    rl2 = np.linalg.norm(got - ref16) / max(np.linalg.norm(ref16), 1e-30)
     assert rl2 <= 2e-3, f"{tag}: bf16 rel L2 {rl2:.3e}"
 
