@@ -80,3 +80,28 @@ def test_value_scale_equivariance(bits, group, e):
     finally:
         base.close()
         scaled.close()
+
+
+@pytest.mark.parametrize("e", [-6, 7])
+@pytest.mark.parametrize("bits,group", [(16, 64), (8, 64), (4, 64), (3, 64), (2, 64)])
+def test_query_scale_cancels_softmax_scale(bits, group, e):
+    """q times 2^e with the softmax scale times 2^-e leaves every score, and so the output,
+    bit-identical: the q copy, the dot products and the group sums of q scale exactly, and
+    scale * log2(e) is scaled by 2^-e exactly.  Fixed partitions, and the matrix engine where
+    it applies (both repeat bit for bit)."""
+    print(f"query scale bits={bits} group={group} e={e}", flush=True)
+    w = make_workload("c3", B=3, len_lo=200, len_hi=1300, bits=bits, group=group)
+    pool = _filled(w, 0)
+    try:
+        q0, q1 = G.u16_dev(w.q_bits), G.u16_dev(_scale_bits(w.q_bits, e))
+        tbl, lens = G.i32_dev(w.table), G.i32_dev(w.lengths)
+        runs = [dict(partition_tokens=128, engine=kvq.ENGINE_VECTOR)]
+        if bits == 4 and group == 64:
+            runs.append(dict(partition_tokens=kvq.PARTITION_STREAM, engine=kvq.ENGINE_MATRIX))
+        for kw in runs:
+            a = kvq.decode(q0, pool, tbl, lens, w.scale, w.max_len, out_f32=True, **kw)
+            b = kvq.decode(q1, pool, tbl, lens, w.scale * 2.0 ** -e, w.max_len, out_f32=True, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(a, b), f"{kw}: scores changed"
+    finally:
+        pool.close()
