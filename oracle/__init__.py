@@ -27,7 +27,9 @@ Pages cited (the text of four npm-diff web pages):
 * "@mlx-bun/inference 0.0.0-stage -> 1.0.0", diff page 134: src/state/paged/cache.ts.
 * "mlx-bun 0.2.0 -> 0.4.0", diff page 47: model/batched-quantized-kv.ts and friends.
 
-Every function here is pinned by ``tests/test_oracle_*.py`` (worked words, closed forms,
-brute force, a library routine); none is "parity unpinned".
+Every public function here is pinned by ``tests/test_oracle_*.py`` (worked words, closed
+forms, brute force, a library routine); the helpers (``bf16.next_up``,
+``quant.levels``, ``attention.workload_kv``) are reached only through a pinned function that
+calls them, so a mistake in one fails that function's pins.  None is "parity unpinned".
 """
 from . import bf16, quant, paged, attention  # noqa: F401

@@ -27,11 +27,6 @@ from . import bf16
 from .paged import Pool, rows_dequantized
 
 
-def visible(length: int, N: int, i: int) -> int:
-    """Tokens row i of N may attend to."""
-    return length - N + i + 1
-
-
 def attend_one(qv: np.ndarray, K: np.ndarray, V: np.ndarray, T: int, scale: float) -> np.ndarray:
     """One query vector against the first T rows of K [len, D] and V [len, DV] (f64); two-pass
     softmax."""
@@ -128,8 +123,3 @@ def workload_output(w, seqs=None) -> np.ndarray:
         kb, vb = workload_kv(w, b)
         K.append(kb), V.append(vb)
     return decode_attention(q, K, V, w.lengths[seqs], w.scale)
-
-
-def to_bf16(x: np.ndarray) -> np.ndarray:
-    """Output rounding: f64 -> f32 -> bf16 (nearest even), as uint16 patterns."""
-    return bf16.rne(np.asarray(x, dtype=np.float64).astype(np.float32))
