@@ -101,11 +101,18 @@ int kv_pool_create(const kvq_pool_desc* desc, kvq_pool** out);
 int kv_pool_wrap(const kvq_pool_desc* desc, void* const planes[KVQ_NUM_PLANES], kvq_pool** out);
 
 /* Release a pool handle (and its planes if the library allocated them).  NULL is a no-op.
- * Work still queued on a stream that reads the pool must finish first. */
+ * Work still queued on a stream that reads the pool must finish first.  The pages' pool
+ * releases its planes the same way ([P134] cache.ts, BlockPool.dispose: scales, biases, keys
+ * and values disposed, the free list emptied), while a view over it releases only what it
+ * holds itself ([P50] paged.ts, pagedAttentionView's dispose) -- here a wrapped pool
+ * (kv_pool_wrap) is such a borrower: only the handle is freed. */
 int kv_pool_destroy(kvq_pool* pool);
 
-/* Device address and size of one plane.  Errors: KVQ_ERR_INVALID for a plane the format
- * lacks. */
+/* Device address and size of one plane, as the pages' pool lists its arrays ([P134] cache.ts,
+ * BlockPool.arrays: keys, values, then keyScales, keyBiases, valueScales, valueBiases where the
+ * format has them).  The pointer is the library's (kv_pool_create) or the caller's (kv_pool_wrap);
+ * it stays valid until kv_pool_destroy.  Errors: KVQ_ERR_INVALID for a NULL argument or a plane
+ * the format lacks (bf16 pages have no scale or bias planes). */
 int kv_pool_plane(const kvq_pool* pool, int32_t plane, void** dev_ptr, size_t* bytes);
 
 /* Copy a pool's descriptor out. */
@@ -160,8 +167,13 @@ typedef struct kvq_decode_shape {
  *   KVQ_ENGINE_AUTO: the vector engine. */
 enum kvq_engine { KVQ_ENGINE_AUTO = 0, KVQ_ENGINE_VECTOR = 1, KVQ_ENGINE_MATRIX = 2 };
 
-/* Bytes of workspace paged_decode_attention needs for this shape (0 if the shape is
- * invalid).  The workspace holds per-partition partial outputs (f32). */
+/* Bytes of workspace paged_decode_attention needs for this shape (0 if the shape is invalid;
+ * kvq_last_error() then says why).  The workspace holds what the pages' direct route allocates
+ * per call and releases after the merge ([P50] paged.ts, pagedAttentionView.attend: the partial
+ * outputs `out` [hq, n, parts, dv] f32 and `normal` [hq, n, parts, 2] f32 -- running max and
+ * normaliser -- disposed in its finally): f32 partial rows (o, m, l) per partition or per
+ * stream slot, and the vector engine's copy of q.  Here the caller owns that memory (e.g. one
+ * torch.empty reused across steps); its content between calls is scratch. */
 size_t paged_decode_workspace_bytes(const kvq_pool* pool, const kvq_decode_shape* shape);
 
 /* Partition size the library uses for this shape: the fixed partition's tokens, or 0 for the
@@ -261,7 +273,11 @@ int kvq_timing_read(int32_t kind, double* avg_ms, int32_t* count);
  * size. */
 int kvq_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
-/* Message for the calling thread's last failing call ("" if none). */
+/* Message for the calling thread's last failing call ("" if none).  The pages fail with a typed
+ * error that carries a message, never a silent truncation ([P134] cache.ts, PagedPoolExhausted:
+ * the pool's block count in the message; [P50] multi-query.ts throws with the offending size);
+ * here the kvq_status code is the type and this string the message.  Thread-local; valid until
+ * the thread's next failing call. */
 const char* kvq_last_error(void);
 
 /* Library version string. */

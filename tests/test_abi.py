@@ -65,7 +65,8 @@ def test_struct_layouts():
 
 
 @pytest.mark.parametrize("name,expect", [("c3", 345157632), ("c2", 139984896), ("c1", 1179648),
-                                         ("c5", 1522151424), ("c4_8", 1140850688), ("c4_2", 335544320)])
+                                         ("c5", 1522151424), ("c4_8", 1140850688), ("c4_2", 335544320),
+                                         ("diag", 603979776)])
 def test_pool_bytes_match_the_layout(lib, name, expect):
     """Pool sizes [NB, HK, BS, width] per plane for the seeded workloads."""
     w = make_workload(name)

@@ -6,7 +6,7 @@ runs it (paged_decode_step: the step's new rows appended at the slots the block 
 the partial pass with the automatic schedule and engine, the merge; for the 4-bit head-dim-256
 workloads also the matrix-core variant).  The oracle cannot take the whole batch in seconds, so the
 check is on sampled sequences (the shortest, the longest and one seeded other; two of the four
-where all four hold 131072 tokens): all their outputs against the oracle (f32 output to max abs /
+where all four hold 131072 tokens; the first, the last and one seeded other where all hold 32768): all their outputs against the oracle (f32 output to max abs /
 rel L2 2e-3, bf16 output within one bf16 ulp or 2e-3), and their pool rows -- codes, scales and
 biases, read back through kv_gather_debug -- against the oracle's quantizer bit for bit."""
 import concurrent.futures
@@ -22,13 +22,15 @@ from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["c2", "c3", "c4_8", "c4_2", "c5"]
+FULL = ["c2", "c3", "c4_8", "c4_2", "c5", "diag"]
 
 
 def _sample(w):
     order = np.argsort(w.lengths, kind="stable")
     if w.B <= 4:                                     # 131072-token sequences: the oracle's minutes
         return sorted({int(order[0]), int(order[-1])})
+    if w.lengths.min() == w.lengths.max():           # equal lengths: first, last and one seeded other
+        return sorted({0, w.B - 1, int(np.random.default_rng(7).integers(1, w.B - 1))})
     rng = np.random.default_rng(7)
     picks = {int(order[0]), int(order[-1]), int(rng.integers(0, w.B))}
     return sorted(picks)

@@ -21,10 +21,10 @@ Recipe (numpy PCG64; every stream keyed by a SeedSequence):
   ``exp(r.uniform(ln 0.5, ln 4, (len_b, HK)))`` scale each row.
 * K, V and q are rounded to bf16 (round to nearest even on the f32 bit pattern).
 
-The five named workloads follow the decode shapes the pages discuss: one-row GQA decode
-over a contiguous 4-bit cache with head dim 256, and paged decode over bf16 or
-affine-quantized pages with a shuffled block table; ``WORKLOADS`` below gives each one's
-shape.
+The named workloads follow the decode shapes the pages discuss: one-row GQA decode
+over a contiguous 4-bit cache with head dim 256 (also at 32k-token contexts in shuffled
+pages), and paged decode over bf16 or affine-quantized pages with a shuffled block table;
+``WORKLOADS`` below gives each one's shape.
 """
 from __future__ import annotations
 
@@ -83,6 +83,10 @@ WORKLOADS = {
     "c4_2": Spec(4, 2, 4, 32, 8, 128, 1, 16, 131072, 131072, 1.0 / math.sqrt(128.0)),
     # 4-bit pages, 64 sequences of 8192..32768 tokens, block 32, GQA 32/4, D 256, 4 query rows
     "c5": Spec(5, 4, 64, 32, 4, 256, 4, 32, 8192, 32768, 1.0 / 16.0, token_norm=True),
+    # the one-row GQA decode shape of the contiguous 4-bit cache (GQA 8/2, D 256) at 32k-token
+    # contexts: 32 sequences of 32768 tokens in shuffled 4-bit pages of 32 tokens (q unscaled,
+    # softmax scale 1/16); K/V N(0,1)
+    "diag": Spec(6, 4, 32, 8, 2, 256, 1, 32, 32768, 32768, 1.0 / 16.0),
 }
 
 
