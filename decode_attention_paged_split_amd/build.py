@@ -53,15 +53,23 @@ def _compile(src: str, obj: str) -> None:
         sys.stderr.write("\n".join(noise) + "\n")
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source and link libkvq.so; returns its path."""
+def build(verbose: bool = True, incremental: bool = False) -> str:
+    """Compile every source and link libkvq.so; returns its path.  incremental: recompile only the
+    sources whose object is older than the source or than any header (a development shortcut)."""
     objdir = os.path.join(ROOT, "_build", "kvq")
     os.makedirs(objdir, exist_ok=True)
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
     objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
-    workers = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
+    todo = list(zip(srcs, objs))
+    if incremental:
+        headers = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")]
+        headers.append(os.path.join(ROOT, "include", "kvq.h"))
+        newest_h = max(os.path.getmtime(h) for h in headers)
+        todo = [(s, o) for s, o in todo if not os.path.exists(o) or
+                os.path.getmtime(o) < max(os.path.getmtime(s), newest_h)]
+    workers = max(1, min(len(todo), int(os.environ.get("MAX_JOBS", "8"))))
     with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
-        list(ex.map(_compile, srcs, objs))
+        list(ex.map(lambda so: _compile(*so), todo))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -75,4 +83,4 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(incremental="--incremental" in sys.argv[1:])
