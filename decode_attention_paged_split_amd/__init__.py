@@ -27,7 +27,8 @@ __all__ = [
     "KvqError", "PoolDesc", "DecodeShape", "Pool", "decode", "lib", "kv_pool_create", "kv_pool_wrap",
     "kv_pool_destroy", "kv_pool_plane_bytes", "kv_append_quantize", "paged_decode_workspace_bytes",
     "paged_decode_partition_tokens", "paged_decode_attention", "paged_decode_partial",
-    "paged_decode_merge", "paged_decode_step", "paged_decode_step_partial", "kv_gather_debug", "make_shape", "gather", "decode_step",
+    "paged_decode_merge", "paged_decode_step", "paged_decode_step_partial", "paged_decode_step_noalloc",
+    "NOALLOC_WORKSPACE_BYTES", "kv_gather_debug", "make_shape", "gather", "decode_step",
     "kvq_timing_enable", "kvq_timing_read", "kvq_probe_read", "TIMING_PREP", "TIMING_PARTIAL", "TIMING_MERGE", "PARTITION_AUTO", "PARTITION_STREAM",
     "PLANES", "LIB_PATH",
 ]
@@ -64,6 +65,7 @@ class DecodeShape(ctypes.Structure):
 ENGINE_AUTO, ENGINE_VECTOR, ENGINE_MATRIX = 0, 1, 2
 TIMING_PREP, TIMING_PARTIAL, TIMING_MERGE = 0, 1, 2
 PARTITION_AUTO, PARTITION_STREAM = 0, -1
+NOALLOC_WORKSPACE_BYTES = 64 * 1024 * 1024     # KVQ_NOALLOC_WORKSPACE_BYTES
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -102,6 +104,8 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.POINTER(DecodeShape), _P, ctypes.c_size_t, _P, _P]),
             "paged_decode_step_partial": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float,
                                                          ctypes.POINTER(DecodeShape), _P, ctypes.c_size_t, _P]),
+            "paged_decode_step_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                                         ctypes.POINTER(DecodeShape), _P, _P]),
             "kv_gather_debug": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                _P * 6, _P]),
             "kvq_probe_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
@@ -224,6 +228,16 @@ def paged_decode_step_partial(q, k_new, v_new, pool: "Pool", block_table, length
     _check(lib().paged_decode_step_partial(_ptr(q), _ptr(k_new), _ptr(v_new), pool.handle, _ptr(block_table),
                                            _ptr(lengths), float(scale), ctypes.byref(shape), _ptr(workspace),
                                            ws_bytes, _stream(stream)))
+
+
+def paged_decode_step_noalloc(q, k_new, v_new, pool: "Pool", block_table, lengths, scale: float,
+                              shape: DecodeShape, out, stream=None) -> None:
+    """paged_decode_step with the library's own device scratch as workspace (no allocation in the
+    call; at most NOALLOC_WORKSPACE_BYTES of workspace; overlapping calls on one device race)."""
+    _need_cuda(q, k_new, v_new, block_table, lengths, out)
+    _check(lib().paged_decode_step_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), pool.handle, _ptr(block_table),
+                                           _ptr(lengths), float(scale), ctypes.byref(shape), _ptr(out),
+                                           _stream(stream)))
 
 
 def paged_decode_partial(q, pool: "Pool", block_table, lengths, scale: float, shape: DecodeShape,

@@ -290,6 +290,15 @@ hipError_t timed(int kind, hipStream_t st, F launch) {
 
 }  // namespace
 
+namespace kvq {
+
+int set_error(int code, const char* msg) {
+  g_err = msg;
+  return code;
+}
+
+}  // namespace kvq
+
 extern "C" {
 
 int kvq_timing_enable(int32_t on) {

@@ -74,6 +74,9 @@ struct MergeArgs {
 // vector takes head_dim / 32 blocks
 constexpr int Q_BLOCK_WORDS = 20;
 
+// records msg as the calling thread's kvq_last_error() and returns code (host side)
+int set_error(int code, const char* msg);
+
 hipError_t launch_append(const AppendArgs& a, int bits, hipStream_t stream);
 // streaming-read probe over bytes (a multiple of 16) of buf with `blocks` workgroups of 256
 hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);

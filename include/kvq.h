@@ -240,6 +240,25 @@ int paged_decode_step_partial(const uint16_t* q, const uint16_t* k_new, const ui
                               const kvq_decode_shape* shape, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* Bytes of the scratch array paged_decode_step_noalloc uses as its workspace (64 MiB). */
+#define KVQ_NOALLOC_WORKSPACE_BYTES (64u * 1024u * 1024u)
+
+/* paged_decode_step for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, layouts, results
+ * and errors as paged_decode_step, without workspace: the partials and the q copy live in a
+ * library-owned device array of KVQ_NOALLOC_WORKSPACE_BYTES bytes, one per device, which that
+ * device holds from the first call on it until the process ends (its address is looked up once
+ * per device, on that first call).  The call itself allocates nothing (no hipMalloc or hipFree, no
+ * allocating library routine; the launch-timing aid, when switched on, creates its events on
+ * first use).  A shape whose paged_decode_workspace_bytes() exceeds KVQ_NOALLOC_WORKSPACE_BYTES is
+ * refused with KVQ_ERR_WORKSPACE before the device is touched.  Every call on a device shares that
+ * device's array and leaves its content behind (no kernel relies on it being zero): calls that
+ * overlap on one device -- on two streams, or from two threads without ordering -- race, and the
+ * caller must serialise them. */
+int paged_decode_step_noalloc(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, kvq_pool* pool,
+                              const int32_t* block_table, const int32_t* lengths, float scale,
+                              const kvq_decode_shape* shape, void* out, void* stream);
+
 /* The fetch copy, for indexing tests ([P134] cache.ts pickBlocks / BlockPool.gather):
  * every plane's rows of each sequence in token order.  out_planes[p] (device) receives
  * plane p as [B, num_kv_heads, max_len, width_p] in the plane's element type; rows at

@@ -305,3 +305,25 @@ def test_matrix_engine_limits(lib):
     h = kvq.kv_pool_wrap(d, [256] * 6)
     assert lib.paged_decode_workspace_bytes(h, ctypes.byref(s)) == 0      # matrix engine: group 64 only
     kvq.kv_pool_destroy(h)
+
+
+def test_noalloc_step_refuses_shapes_beyond_its_scratch(lib):
+    """paged_decode_step_noalloc checks the shape's workspace against its built-in scratch before it
+    touches the device: too large is KVQ_ERR_WORKSPACE, an invalid shape the allocating entry
+    point's own code, a NULL pointer KVQ_ERR_INVALID."""
+    src = open(HEADER).read()
+    m = re.search(r"#define KVQ_NOALLOC_WORKSPACE_BYTES \((\d+)u \* 1024u \* 1024u\)", src)
+    assert m and int(m.group(1)) << 20 == kvq.NOALLOC_WORKSPACE_BYTES
+    p = _FakePool(NB=4096)
+    P = ctypes.c_void_p(256)
+    big = kvq.DecodeShape(4096, 16, 4, 1100, 32768, 0, 0, 0)
+    need = lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(big))
+    assert need > kvq.NOALLOC_WORKSPACE_BYTES
+    assert lib.paged_decode_step_noalloc(P, P, P, p.handle, P, P, 1.0, ctypes.byref(big), P, None) == -5
+    assert "KVQ_NOALLOC_WORKSPACE_BYTES" in lib.kvq_last_error().decode()
+    bad = kvq.DecodeShape(2, 16, 129, 40, 1000, 0, 0, 0)
+    assert lib.paged_decode_step_noalloc(P, P, P, p.handle, P, P, 1.0, ctypes.byref(bad), P, None) == -2
+    ok = kvq.DecodeShape(2, 16, 1, 40, 1000, 0, 0, 0)
+    assert 0 < lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(ok)) <= kvq.NOALLOC_WORKSPACE_BYTES
+    assert lib.paged_decode_step_noalloc(P, None, P, p.handle, P, P, 1.0, ctypes.byref(ok), P, None) == -1
+    p.close()
