@@ -135,7 +135,8 @@ int choose_partition(const kvq_pool* pool, const kvq_decode_shape* s) {
 
 // Stream schedule: the most ranges the stream is cut into and the partial slots per (unit, range).
 // Every range's waves are resident at once.  The vector engine launches one workgroup of 8 waves
-// (two per SIMD) per compute unit, whose waves share its range's tiles.  The matrix engine runs two
+// (two per SIMD) per compute unit, whose waves share its range's tiles: a slot per (unit, range,
+// wave), of which the range's last unit uses only the first (its waves combine in LDS).  The matrix engine runs two
 // waves per SIMD: at head dim 256 a workgroup of two waves (one per half of the head dim) works one
 // range, 4 workgroups per compute unit; at head dim 128 each of 8 waves per compute unit works a
 // range of its own.  KVQ_MFMA_RANGES_PER_CU overrides the 4 / 8, for sweeps.
@@ -545,6 +546,7 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   m.len_cap = a.len_cap;
   m.batch = shape->batch; m.HK = d.num_kv_heads; m.qgroups = a.qgroups; m.qvw = P->qvw;
   m.num_ranges = a.num_ranges; m.range_sub = a.range_sub; m.min_tokens = a.min_tokens;
+  m.stream_combined = (pt == 0 && !P->mfma) ? 1 : 0;
   return KVQ_OK;
 }
 

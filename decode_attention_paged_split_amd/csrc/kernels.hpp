@@ -67,6 +67,7 @@ struct MergeArgs {
   int32_t HQ, N, D, part_tokens, num_parts, out_f32, max_len;
   int32_t len_cap;          // min(max_len, max_blocks * BS): lengths are clamped to [0, len_cap]
   int32_t batch, HK, qgroups, qvw, num_ranges, range_sub, min_tokens;   // stream (part_tokens == 0)
+  int32_t stream_combined;  // stream: a range's waves combined their partials of its last unit
 };
 
 // words per block of the vector engine's q copy: 16 bf16 pairs of one query vector, then (last

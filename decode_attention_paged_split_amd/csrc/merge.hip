@@ -14,7 +14,8 @@
 // Output is bf16 (round to nearest even) or f32.
 // Stream schedule: the stream of T tokens is cut into R = min(num_ranges, ceil(T / min_tokens))
 // ranges; a unit's partials sit in range_sub consecutive slots per range it meets, from slot
-// (unit + first range) * range_sub on.
+// (unit + first range) * range_sub on -- or (stream_combined) in the first of them only, for
+// every range whose end lies inside the unit (its waves combined their partials).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -34,9 +35,12 @@ __global__ void __launch_bounds__(NT) merge_kernel(MergeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int len = max(0, min(a.lengths[b], a.len_cap));
 
-  // where partition p of this row lives
-  int nparts = 0;
-  int64_t mbase = 0, obase = 0, mstride = 2, ostride = a.D;
+  // where partition p of this row lives: fixed partitions at mbase + p * mstride (and obase +
+  // p * ostride); stream slots from slot0 on, one per (range, wave), except that (combined) the
+  // ranges before the last one the unit meets hold one partial each and so may the last one
+  int nparts = 0, nr = 0;
+  int64_t mbase = 0, obase = 0, mstride = 2, ostride = a.D, slot0 = 0, slot_last = 0;
+  bool by_slot = false;
   if (a.part_tokens > 0) {
     nparts = len > 0 ? min((len + a.part_tokens - 1) / a.part_tokens, a.num_parts) : 0;
     mbase = (int64_t)row * a.num_parts * 2;
@@ -66,10 +70,20 @@ __global__ void __launch_bounds__(NT) merge_kernel(MergeArgs a) {
       const int64_t start = (int64_t)pre * HQG + (int64_t)(hk * a.qgroups + qg) * len;
       const int64_t end = start + len;
       const int64_t w_first = start * weff / T, w_last = (end - 1) * weff / T;
-      nparts = (int)(w_last - w_first + 1) * a.range_sub;
-      const int64_t slot0 = (u + w_first) * a.range_sub;
-      mbase = (slot0 * a.qvw + j) * 2;
-      obase = (slot0 * a.qvw + j) * a.D;
+      if (a.stream_combined) {
+        // a range whose end lies inside the unit combined its waves' partials into one (every
+        // range before the last; the last too if it ends where the unit ends)
+        const int64_t x1_last = ((w_last + 1) * T + weff - 1) / weff;
+        nr = (int)(w_last - w_first);
+        nparts = nr + (x1_last == end ? 1 : a.range_sub);
+      } else {
+        nparts = (int)(w_last - w_first + 1) * a.range_sub;
+      }
+      slot0 = (u + w_first) * a.range_sub;
+      slot_last = (u + w_last) * a.range_sub;
+      by_slot = true;
+      mbase = j * 2;
+      obase = (int64_t)j * a.D;
       mstride = (int64_t)a.qvw * 2;
       ostride = (int64_t)a.qvw * a.D;
     }
@@ -85,8 +99,13 @@ __global__ void __launch_bounds__(NT) merge_kernel(MergeArgs a) {
     const float* mb = a.ml + mbase;
 #pragma unroll 4
     for (int p = sidx; p < nparts; p += S) {
-      const float2 ml = *reinterpret_cast<const float2*>(mb + p * mstride);
-      const float4 o = *reinterpret_cast<const float4*>(ob + p * ostride);
+      int64_t q = p;                                           // slot (stream) or partition
+      if (by_slot) {
+        if (!a.stream_combined) q = slot0 + p;
+        else q = p < nr ? slot0 + (int64_t)p * a.range_sub : slot_last + (p - nr);
+      }
+      const float2 ml = *reinterpret_cast<const float2*>(mb + q * mstride);
+      const float4 o = *reinterpret_cast<const float4*>(ob + q * ostride);
       // branch-free, so every load is issued ahead of the arithmetic; a skipped partial
       // (m = -inf) contributes through selects only, so its unwritten l and o are never used
       const bool ok = ml.x != -INFINITY;

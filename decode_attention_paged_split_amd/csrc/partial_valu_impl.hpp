@@ -49,9 +49,11 @@
 //    workgroup per compute unit).  The waves share the range's 64-token tiles through an LDS
 //    counter: the two waves on a SIMD do not progress at the same rate (the older one has
 //    issue priority), and a static split would leave the slower one running alone at the
-//    end.  Each wave writes one partial per unit of its range, at slot (unit + r) * 8 + wave
-//    (distinct for every (unit, range, wave) because ranges are contiguous and ordered), so
-//    partials stay few whatever the length mix.
+//    end.  Each wave writes one partial per unit that ends inside its range, at slot
+//    (unit + r) * 8 + wave (distinct for every (unit, range, wave) because ranges are contiguous
+//    and ordered); for the range's last unit the 8 waves' partials are combined in LDS first and
+//    written once, at slot (unit + r) * 8.  (A combine at every unit's end would need a barrier
+//    there, and the waves that took one tile fewer of the unit would wait a whole tile.)
 #pragma once
 
 #include "append_rows.hpp"
@@ -810,7 +812,15 @@ template <int BITS, int D, int DV, int QVW, int GS>
 __global__ void __launch_bounds__(VALU_STREAM_WAVES * 64, 1)
 partial_stream_kernel(PartialArgs a) {
   constexpr int NW = VALU_STREAM_WAVES;
-  __shared__ __align__(16) WaveScratch<BITS, DV, QVW, GS> ws[NW];
+  // the waves' tile scratch; between units (after a barrier) the waves' partials of the unit
+  // just finished, for the combine
+  __shared__ __align__(16) union {
+    WaveScratch<BITS, DV, QVW, GS> ws[NW];
+    struct {
+      float o[NW][QVW][DV];
+      float m[NW][QVW], l[NW][QVW];
+    } comb;
+  } sh;
   __shared__ int tile_ctr;                                       // next tile of the range
 
   const int lane = threadIdx.x & 63;
@@ -863,8 +873,10 @@ partial_stream_kernel(PartialArgs a) {
 
   // The range is a list of tiles: unit by unit, the unit's part of the range cut into 64-token
   // tiles.  The workgroup's waves take tiles from one LDS counter, so faster waves take more of
-  // them; every wave walks every unit of the range and writes one partial for it (possibly
-  // empty) at slot (unit + range) * NW + wave.
+  // them; every wave walks every unit of the range.  For a unit that ends inside the range each
+  // wave writes its own partial (possibly empty) at slot (unit + range) * NW + wave; the range's
+  // last unit, whose tiles end with the range, has its waves' partials combined in LDS and written
+  // once, at slot (unit + range) * NW (a barrier there costs nothing: every wave is done).
   auto take = [&]() {
     int k = 0;
     if (lane == 0) k = atomicAdd(&tile_ctr, 1);
@@ -892,24 +904,58 @@ partial_stream_kernel(PartialArgs a) {
           kq = take();
           return t0u + (k - kb) * PV_TILE;
         },
-        ws[wave], st, lane);
+        sh.ws[wave], st, lane);
     kq = uni(kq);
-    const int64_t slot = (un.u + g) * NW + wave;
-    acc_write<BITS, DV, QVW, GS>(
-        st, lane, [&](int j) { return opart + (slot * QVW + j) * DV; },
-        [&](int j, float m, float l) { ml[(slot * QVW + j) * 2] = m; ml[(slot * QVW + j) * 2 + 1] = l; });
-    kbase += ntiles;
-    x += seg;
-    t_lo += seg;
-    if (t_lo >= len && x < x1) {
-      t_lo = 0;
-      if (++uu == HQG) {
-        uu = 0;
-        do { ++b; } while (b < B && clamp_len(a, b) == 0);
-        if (b >= B) break;                                       // (x1 <= T: not reached)
-        len = uni(clamp_len(a, b));
+    const int64_t slot = (un.u + g) * NW;
+    if (x + seg < x1) {
+      // a unit that ends inside the range: one partial per wave (no barrier: the waves that are
+      // done with its tiles go on to the next unit)
+      acc_write<BITS, DV, QVW, GS>(
+          st, lane, [&](int j) { return opart + ((slot + wave) * QVW + j) * DV; },
+          [&](int j, float m, float l) {
+            ml[((slot + wave) * QVW + j) * 2] = m; ml[((slot + wave) * QVW + j) * 2 + 1] = l;
+          });
+      kbase += ntiles;
+      x += seg;
+      t_lo += seg;
+      if (t_lo >= len) {
+        t_lo = 0;
+        if (++uu == HQG) {
+          uu = 0;
+          do { ++b; } while (b < B && clamp_len(a, b) == 0);
+          if (b >= B) break;                                     // (x1 <= T: not reached)
+          len = uni(clamp_len(a, b));
+        }
       }
+      continue;
     }
+    // the range's last unit: every wave is done, so the waves' partials combine in LDS (log-sum-exp)
+    // into one, written at the unit's first slot of the range
+    __syncthreads();
+    acc_write<BITS, DV, QVW, GS>(
+        st, lane, [&](int j) { return &sh.comb.o[wave][j][0]; },
+        [&](int j, float m, float l) { sh.comb.m[wave][j] = m; sh.comb.l[wave][j] = l; });
+    __syncthreads();
+    for (int e = threadIdx.x; e < QVW * DV; e += NW * 64) {
+      const int j = e / DV, d = e - j * DV;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, sh.comb.m[w][j]);
+      float num = 0.0f, den = 0.0f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float mw = sh.comb.m[w][j];
+          if (mw == -INFINITY) continue;
+          const float f = fast_exp2(mw - M);
+          num = fmaf(f, sh.comb.o[w][j][d], num);
+          den = fmaf(f, sh.comb.l[w][j], den);
+        }
+      }
+      opart[(slot * QVW + j) * DV + d] = num;
+      if (d == 0) { ml[(slot * QVW + j) * 2] = M; ml[(slot * QVW + j) * 2 + 1] = den; }
+    }
+    break;
   }
 }
 
