@@ -66,8 +66,9 @@ partial_mfma_kernel(PartialArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float m = -INFINITY, l = 0.0f, pbias[G];
+    int ve[G];                                       // V groups' prescale exponents
 #pragma unroll
-    for (int g = 0; g < G; ++g) pbias[g] = 0.0f;
+    for (int g = 0; g < G; ++g) { pbias[g] = 0.0f; ve[g] = MF_VE_NONE; }
 
     // ---- tile pipeline: while tile i is computed, the K rows, V rows and scales of tile i + 1
     // are in flight, and the block-table entries of tile i + 2 one step earlier still.  Lane r
@@ -94,11 +95,24 @@ partial_mfma_kernel(PartialArgs a) {
 #pragma unroll
       for (int i = 0; i < NVL; ++i)
         *reinterpret_cast<u32x4*>(&S.v[(64 / CPR) * i + lane / CPR][16 * (lane % CPR)]) = cur.v[i];
+      {
+        bool moves = false;
+#pragma unroll
+        for (int g = 0; g < G; ++g) moves |= mf_vpre_moves(mf_bf16(cur.vs, g), ve[g]);
+        if (__ballot(moves)) {                          // uniform; a segment's first tile
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float r = mf_vpre_update(mf_bf16(cur.vs, g), ve[g]);
+#pragma unroll
+            for (int dt = g * (DT / G); dt < (g + 1) * (DT / G); ++dt) o[dt] *= r;
+          }
+        }
+      }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float ksc = mf_bf16(cur.ks, g), kbi = mf_bf16(cur.kb, g);
         S.ksb[lane][g] = make_float2(ksc, fmaf(-128.0f, ksc, kbi));
-        S.vs[g][lane] = mf_bf16(cur.vs, g);
+        S.vs[g][lane] = mf_bf16(cur.vs, g) * mf_pow2(-ve[g]);
         S.vb[g][lane] = mf_bf16(cur.vb, g);
       }
 #pragma unroll
@@ -242,9 +256,10 @@ partial_mfma_kernel(PartialArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const float pbv = pbias[dt / (DT / G)];
+        const float sc = mf_pow2(ve[dt / (DT / G)]);   // the weights' prescale
         constexpr float two24 = 16777216.0f;        // the V codes entered as c * 2^-24
-        const float4 v4 = make_float4(fmaf(o[dt][0], two24, pbv), fmaf(o[dt][1], two24, pbv),
-                                      fmaf(o[dt][2], two24, pbv), fmaf(o[dt][3], two24, pbv));
+        const float4 v4 = make_float4(fmaf(o[dt][0] * sc, two24, pbv), fmaf(o[dt][1] * sc, two24, pbv),
+                                      fmaf(o[dt][2] * sc, two24, pbv), fmaf(o[dt][3] * sc, two24, pbv));
         *reinterpret_cast<float4*>(orow + 16 * dt + 4 * ks) = v4;
       }
       if (ks == 0) {

@@ -26,9 +26,11 @@
 //  * P.V: v_mfma_f32_16x16x32_f16 with A = V^T and B = (p * scale)^T.  V^T comes straight from
 //    the raw 4-bit tile in LDS through ds_read_b64_tr_b4 (a 16 x 16 nibble transpose per 16
 //    lanes); its codes enter as f16 subnormals (bits c = value c * 2^-24, exact, one AND per
-//    pair) and the accumulators are scaled by 2^24 at the end.  The weight w = p * s(token, group) is split into f16 hi + lo (rounded to nearest),
-//    two MFMAs per step, so the product is accurate to ~2^-22 relative; the bias term
-//    sum_t p * b is accumulated per (vector, group) in f32 and added at the end.
+//    pair) and the accumulators are scaled by 2^24 at the end.  The weight w = p * s(token, group),
+//    prescaled by a power of two per group (mf_vpre_update), is split into f16 hi + lo (rounded
+//    to nearest), two MFMAs per step, so the product is accurate to ~2^-22 relative whatever the
+//    V scale; the bias term sum_t p * b is accumulated per (vector, group) in f32 and added at
+//    the end.
 //  * loads: the K rows, V rows and scales of tile i + 1 are in flight while tile i is computed.
 
 //
@@ -129,6 +131,35 @@ __device__ __forceinline__ void split_f16(float w0, float w1, uint32_t& hi, uint
   const f16x2 h2 = pk_f16(w0, w1);
   hi = __builtin_bit_cast(uint32_t, h2);
   lo = __builtin_bit_cast(uint32_t, pk_f16(w0 - (float)h2[0], w1 - (float)h2[1]));
+}
+
+// Power-of-two prescale of the P.V weights before their f16 split, per V scale group: the weights
+// enter as w * 2^-E, E the group's exponent, so that the largest sit near 2^14 whatever the V scale
+// (hi and lo then both stay normal and keep ~22 bits, and hi never overflows: a tile's V scales stay
+// below 2^(E+7) and p <= 2^8 with the lazy running max, so w * 2^-E < 2^15).  E starts unset, is
+// taken from the first tile's largest scale and only grows: when a tile's scale passes 2^(E+7) the
+// group's accumulators are multiplied by 2^(E_old - E_new), exactly, and E moves.  The output
+// takes the factor 2^E back at the end, exactly.
+constexpr int MF_VE_NONE = -1000;
+
+__device__ __forceinline__ float mf_pow2(int k) { return __int_as_float(max(k + 127, 1) << 23); }
+
+// whether this lane's V scale s needs the group's prescale to move (E unset, or s > 2^(E+7))
+__device__ __forceinline__ bool mf_vpre_moves(float s, int e) {
+  return e == MF_VE_NONE || s > mf_pow2(e + 7);
+}
+
+// the whole wave: move the group's exponent e to cover every lane's scale s; returns the factor
+// (<= 1) by which the group's accumulators must be multiplied
+__device__ __forceinline__ float mf_vpre_update(float s, int& e) {
+  const float smax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+      __builtin_bit_cast(int, block_reduce<OpMax, 1, 64>(s))));
+  if (e != MF_VE_NONE && smax <= mf_pow2(e + 7)) return 1.0f;
+  // smax < 2^f, f its frexp exponent: with E = f - 7, smax * 2^-E < 2^7
+  const int en = max(__builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(smax)) - 7, -100);
+  const float r = (e == MF_VE_NONE) ? 1.0f : mf_pow2(e - en);
+  e = en;
+  return r;
 }
 
 // 4 x 4 transpose of dwords across the four 16-lane rows of a wave: on entry register j of row

@@ -59,6 +59,7 @@ partial_mfma_split_kernel(PartialArgs a) {
 #pragma unroll
     for (int dt = 0; dt < SP_DT; ++dt) o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float m = -INFINITY, l = 0.0f, pbias[SP_G] = {0.0f, 0.0f};
+    int ve[SP_G] = {MF_VE_NONE, MF_VE_NONE};         // this wave's V groups' prescale exponents
 
     // ---- tile pipeline as in the single-wave kernel: tile i + 1's loads in flight during tile i
     auto tab_idx = [&](int tstart) -> int {
@@ -90,8 +91,14 @@ partial_mfma_split_kernel(PartialArgs a) {
         const float ks0 = bf16_lo(cur.ks), ks1 = bf16_hi(cur.ks);
         *reinterpret_cast<float4*>(&S.ksb[lane][0]) =
             make_float4(ks0, fmaf(-128.0f, ks0, bf16_lo(cur.kb)), ks1, fmaf(-128.0f, ks1, bf16_hi(cur.kb)));
-        S.vs[0][lane] = bf16_lo(cur.vs);
-        S.vs[1][lane] = bf16_hi(cur.vs);
+        if (__ballot(mf_vpre_moves(bf16_lo(cur.vs), ve[0]) || mf_vpre_moves(bf16_hi(cur.vs), ve[1]))) {
+          const float r0 = mf_vpre_update(bf16_lo(cur.vs), ve[0]);   // uniform; a segment's first tile
+          const float r1 = mf_vpre_update(bf16_hi(cur.vs), ve[1]);
+#pragma unroll
+          for (int dt = 0; dt < SP_DT; ++dt) o[dt] *= (dt < SP_DT / SP_G) ? r0 : r1;
+        }
+        S.vs[0][lane] = bf16_lo(cur.vs) * mf_pow2(-ve[0]);
+        S.vs[1][lane] = bf16_hi(cur.vs) * mf_pow2(-ve[1]);
         S.vb[0][lane] = bf16_lo(cur.vb);
         S.vb[1][lane] = bf16_hi(cur.vb);
       }
@@ -231,8 +238,9 @@ partial_mfma_split_kernel(PartialArgs a) {
 #pragma unroll
       for (int dt = 0; dt < SP_DT; ++dt) {
         const float pbv = pbias[dt / (SP_DT / SP_G)];
-        const float4 v4 = make_float4(fmaf(o[dt][0], two24, pbv), fmaf(o[dt][1], two24, pbv),
-                                      fmaf(o[dt][2], two24, pbv), fmaf(o[dt][3], two24, pbv));
+        const float sc = mf_pow2(ve[dt / (SP_DT / SP_G)]);   // the weights' prescale
+        const float4 v4 = make_float4(fmaf(o[dt][0] * sc, two24, pbv), fmaf(o[dt][1] * sc, two24, pbv),
+                                      fmaf(o[dt][2] * sc, two24, pbv), fmaf(o[dt][3] * sc, two24, pbv));
         *reinterpret_cast<float4*>(orow + 16 * dt + 4 * ks) = v4;
       }
       if (h == 0 && ks == 0) {

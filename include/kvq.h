@@ -160,7 +160,9 @@ typedef struct kvq_decode_shape {
  * paged_decode_attention.
  *   KVQ_ENGINE_VECTOR: vector ALU -- v_dot2_f32_bf16 for q.k, f32 FMA for P.V; every format.
  *   KVQ_ENGINE_MATRIX: matrix cores -- q.k with exact bf16 products, P.V with exact f16 codes
- *     against the weight split into two f16 halves (~2^-22 relative); 4-bit pages, head_dim
+ *     against the weight split into two f16 halves (~2^-22 relative, at any V scale: the weights
+ *     are prescaled by a power of two per scale group and the factor taken back exactly, so the
+ *     output on V times 2^e is exactly 2^e times the output on V); 4-bit pages, head_dim
  *     128 or 256 (v_head_dim the same), the balanced stream only (partition_tokens <= 0).  It serves the GQA groups where the vector ALU
  *     rather than HBM bounds the pass ([P50] multi-query.ts puts a KV head's query rows on the
  *     matrix unit for the same reason).
