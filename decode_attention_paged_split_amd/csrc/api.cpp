@@ -234,9 +234,11 @@ WsLayout workspace_layout(const kvq_pool* pool, const kvq_decode_shape* s, int p
   L.ml_off = up(rows * pool->desc.v_head_dim * sizeof(float));
   L.qp_off = L.total = L.ml_off + rows * 2 * sizeof(float);
   if (!use_mfma(s)) {
+    // the q copy, then kvq::Q_COPY_TAIL bytes the partial kernel's scalar-cache warm-up may read
+    // past the last unit's copy (it requests whole groups of 64-byte lines)
     const size_t qv = (size_t)s->batch * pool->desc.num_kv_heads * qgroups_of(pool, s) * qvw_of(pool, s);
     L.qp_off = up(L.total);
-    L.total = L.qp_off + qv * (pool->desc.head_dim / 32) * kvq::Q_BLOCK_WORDS * 4;
+    L.total = L.qp_off + qv * (pool->desc.head_dim / 32) * kvq::Q_BLOCK_WORDS * 4 + kvq::Q_COPY_TAIL;
   }
   return L;
 }

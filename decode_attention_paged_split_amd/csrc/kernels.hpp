@@ -74,6 +74,9 @@ struct MergeArgs {
 // block of a scale group, affine pages) the f32 sum of q over the group, then padding; a query
 // vector takes head_dim / 32 blocks
 constexpr int Q_BLOCK_WORDS = 20;
+// bytes of workspace after the q copy: the partial kernel warms the scalar cache with a unit's copy
+// in groups of eight 64-byte lines, which may reach up to seven lines past the last unit's copy
+constexpr int Q_COPY_TAIL = 512;
 
 // records msg as the calling thread's kvq_last_error() and returns code (host side)
 int set_error(int code, const char* msg);

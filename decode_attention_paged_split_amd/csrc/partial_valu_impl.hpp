@@ -397,7 +397,31 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
     for (int c = 0; c < KCPV; ++c) *reinterpret_cast<u32x4*>(&ws.v[lane][16 * c]) = src.c[c];
   };
 
-  // ---- prologue: rows, K and V part 0 and scales of the first tile
+  // ---- prologue: the unit's q copy into the scalar cache (eight 64-byte lines requested per wait:
+  // the K phase asks for its blocks one after the other and would wait for every line's first miss
+  // in turn; the last group may reach past the copy, into the next unit's or the workspace's
+  // Q_COPY_TAIL bytes), then rows, K and V part 0 and scales of the first tile
+  {
+    constexpr int QL = (G * NHB * QVW * QBS + 15) / 16;           // 64-byte lines of the q copy
+#pragma unroll
+    for (int c = 0; c < QL; c += 8) {
+      const scalar_u32* base = qu + 16 * c;
+      typedef int i32x16 __attribute__((ext_vector_type(16)));
+      i32x16 sink;
+      // the loads land in the same 16 registers (values unused) and are waited for in this block
+      asm volatile(
+          "s_load_dwordx16 %0, %1, 0x0\n\t"
+          "s_load_dwordx16 %0, %1, 0x40\n\t"
+          "s_load_dwordx16 %0, %1, 0x80\n\t"
+          "s_load_dwordx16 %0, %1, 0xc0\n\t"
+          "s_load_dwordx16 %0, %1, 0x100\n\t"
+          "s_load_dwordx16 %0, %1, 0x140\n\t"
+          "s_load_dwordx16 %0, %1, 0x180\n\t"
+          "s_load_dwordx16 %0, %1, 0x1c0\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&s"(sink) : "s"(base) : "memory");
+    }
+  }
   int row = row_of(min(tt + lane, t1 - 1), table_entry(min(tt + lane, t1 - 1)));
   RowPart<KCP> kcur = load_row_part<KCP>(kplane, row, ROWB, 0);
   Scales<G, GV> sc, scn;
@@ -814,13 +838,11 @@ partial_stream_kernel(PartialArgs a) {
   constexpr int NW = VALU_STREAM_WAVES;
   // the waves' tile scratch; between units (after a barrier) the waves' partials of the unit
   // just finished, for the combine
-  __shared__ __align__(16) union {
-    WaveScratch<BITS, DV, QVW, GS> ws[NW];
-    struct {
-      float o[NW][QVW][DV];
-      float m[NW][QVW], l[NW][QVW];
-    } comb;
-  } sh;
+  // the waves' tile scratch; a wave done with the range's last unit puts its partial of it in its
+  // own scratch for the combine: [QVW][DV] o, then [QVW] m, then [QVW] l
+  __shared__ __align__(16) WaveScratch<BITS, DV, QVW, GS> ws[NW];
+  static_assert(sizeof(WaveScratch<BITS, DV, QVW, GS>) >= (QVW * DV + 2 * QVW) * sizeof(float),
+                "a wave's partial fits its scratch");
   __shared__ int tile_ctr;                                       // next tile of the range
 
   const int lane = threadIdx.x & 63;
@@ -904,7 +926,7 @@ partial_stream_kernel(PartialArgs a) {
           kq = take();
           return t0u + (k - kb) * PV_TILE;
         },
-        sh.ws[wave], st, lane);
+        ws[wave], st, lane);
     kq = uni(kq);
     const int64_t slot = (un.u + g) * NW;
     if (x + seg < x1) {
@@ -929,27 +951,31 @@ partial_stream_kernel(PartialArgs a) {
       }
       continue;
     }
-    // the range's last unit: every wave is done, so the waves' partials combine in LDS (log-sum-exp)
-    // into one, written at the unit's first slot of the range
+    // the range's last unit: each wave, done with its tiles, puts its partial in its own scratch;
+    // once all are there they combine (log-sum-exp) into one, written at the unit's first slot of
+    // the range
+    {
+      float* mine = reinterpret_cast<float*>(&ws[wave]);
+      acc_write<BITS, DV, QVW, GS>(
+          st, lane, [&](int j) { return mine + j * DV; },
+          [&](int j, float m, float l) { mine[QVW * DV + j] = m; mine[QVW * DV + QVW + j] = l; });
+    }
     __syncthreads();
-    acc_write<BITS, DV, QVW, GS>(
-        st, lane, [&](int j) { return &sh.comb.o[wave][j][0]; },
-        [&](int j, float m, float l) { sh.comb.m[wave][j] = m; sh.comb.l[wave][j] = l; });
-    __syncthreads();
+    auto part = [&](int w) { return reinterpret_cast<const float*>(&ws[w]); };
     for (int e = threadIdx.x; e < QVW * DV; e += NW * 64) {
       const int j = e / DV, d = e - j * DV;
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, sh.comb.m[w][j]);
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, part(w)[QVW * DV + j]);
       float num = 0.0f, den = 0.0f;
       if (M != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-          const float mw = sh.comb.m[w][j];
+          const float mw = part(w)[QVW * DV + j];
           if (mw == -INFINITY) continue;
           const float f = fast_exp2(mw - M);
-          num = fmaf(f, sh.comb.o[w][j][d], num);
-          den = fmaf(f, sh.comb.l[w][j], den);
+          num = fmaf(f, part(w)[j * DV + d], num);
+          den = fmaf(f, part(w)[QVW * DV + QVW + j], den);
         }
       }
       opart[(slot * QVW + j) * DV + d] = num;

@@ -210,10 +210,11 @@ def _up(x):
 
 def _ws_bytes(rows, D, qvecs=0, affine=True):
     """partials: rows of D floats (padded to 256 B) + rows of (max, normaliser); then the vector
-    engine's q copy (per query vector D/32 blocks of 20 words)"""
+    engine's q copy (per query vector D/32 blocks of 20 words) and 512 bytes the partial kernel may
+    read past it"""
     total = _up(rows * D * 4) + rows * 2 * 4
     if qvecs:
-        total = _up(total) + qvecs * (D // 32) * 20 * 4
+        total = _up(total) + qvecs * (D // 32) * 20 * 4 + 512    # + the q copy's 512-byte tail
     return total
 
 
