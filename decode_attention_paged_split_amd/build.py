@@ -2,7 +2,8 @@
 
     python -m decode_attention_paged_split_amd.build
 
-compiles csrc/*.hip and csrc/*.cpp with hipcc and links libkvq.so next to this file.
+compiles csrc/*.hip and csrc/*.cpp with hipcc and links libkvq.so next to this file;
+``--sanitize`` links _build/sanitize/libkvq_san.so, whose host code runs under ASan + UBSan.
 Every HIP translation unit is built with packed-FP32 instructions disabled (the
 compiler then never emits v_pk_{add,mul,fma}_f32).
 """
@@ -82,5 +83,68 @@ def build(verbose: bool = True, incremental: bool = False) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the C ABI's host code (argument
+# validation, pool handles, workspace carving, the per-device scratch table), for CPU tests.  Only
+# the host pass is instrumented (every sanitizer flag follows -Xarch_host); device code is unchanged.
+SAN_SOURCES = ("api.cpp", "noalloc.hip")
+SAN_FLAGS = ["-O1", "-g",
+             "-Xarch_host", "-fsanitize=address",
+             "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(ROOT, "_build", "sanitize", "libkvq_san.so")
+
+
+def asan_runtime() -> str:
+    """The shared AddressSanitizer runtime of ROCm's clang (a process loading the sanitized library
+    needs it preloaded, since the Python interpreter is not instrumented)."""
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        import glob
+        found = sorted(glob.glob("/opt/rocm*/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+        if not found:
+            raise RuntimeError("the shared AddressSanitizer runtime was not found")
+        path = found[-1]
+    return path
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    """Link SAN_LIB from the sanitized host sources and the regular objects of the other sources
+    (built by build() first when missing); returns its path."""
+    objdir = os.path.join(ROOT, "_build", "kvq")
+    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+    plain = [os.path.join(objdir, f + ".o") for f in srcs if f not in SAN_SOURCES]
+    if not all(os.path.exists(o) for o in plain):
+        build(verbose=verbose, incremental=True)
+    sandir = os.path.dirname(SAN_LIB)
+    os.makedirs(sandir, exist_ok=True)
+    san = []
+    for f in SAN_SOURCES:
+        src, obj = os.path.join(CSRC, f), os.path.join(sandir, f + ".o")
+        cmd = [_hipcc()] + [c for c in COMMON if c != "-O3"] + SAN_FLAGS
+        if f.endswith(".hip"):
+            cmd += DEVICE + ["-x", "hip"]
+        r = subprocess.run(cmd + ["-c", src, "-o", obj], capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"sanitized compile of {f} failed")
+        san.append(obj)
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libasan",
+           "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined",
+           "-o", SAN_LIB] + plain + san
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("link of the sanitized library failed")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build(incremental="--incremental" in sys.argv[1:])
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized()
+    else:
+        build(incremental="--incremental" in sys.argv[1:])
