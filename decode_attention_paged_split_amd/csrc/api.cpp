@@ -155,6 +155,20 @@ StreamGeom stream_geom(const kvq_pool* pool, const kvq_decode_shape* s) {
   return {device_cus(), kvq::VALU_STREAM_WAVES, kvq::VALU_STREAM_WAVES * kvq::VALU_TILE};
 }
 
+// Vector-engine stream: the query groups of one KV head worked side by side on one range, by L
+// workgroups on one XCD (one group each), so that each K/V row is fetched from memory once for
+// all of them: 4 when the groups come in fours, 2 when in pairs, else 1.  KVQ_STREAM_LANES (1, 2 or 4,
+// dividing the group count) overrides, for measurements.
+int stream_lanes(int qgroups, int pt, bool mfma) {
+  if (pt != 0 || mfma) return 1;
+  int L = qgroups % 4 == 0 ? 4 : (qgroups % 2 == 0 ? 2 : 1);
+  if (const char* e = std::getenv("KVQ_STREAM_LANES")) {
+    const int v = std::atoi(e);
+    if ((v == 1 || v == 2 || v == 4) && qgroups % v == 0) L = v;
+  }
+  return L;
+}
+
 // query vectors per workgroup (vector ALU) or per wave (matrix cores, padded to 16)
 int qvw_of(const kvq_pool* pool, const kvq_decode_shape* s) {
   const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
@@ -536,6 +550,8 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   a.len_cap = (int)std::min<long>(shape->max_len, (long)shape->max_blocks_per_seq * d.block_size);
   const StreamGeom sg = stream_geom(pool, shape);
   a.batch = shape->batch; a.num_ranges = sg.ranges; a.range_sub = sg.sub; a.min_tokens = sg.min_tokens;
+  a.lanes = stream_lanes(a.qgroups, pt, P->mfma);
+  if (a.lanes > 1) a.num_ranges = std::max(1, a.num_ranges / a.lanes);   // L workgroups per range
 
   P->merge_threads = merge_threads_for(d.v_head_dim, pt, parts, sg,
                                        (double)shape->batch * d.num_kv_heads * a.qgroups,
@@ -549,6 +565,7 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   m.batch = shape->batch; m.HK = d.num_kv_heads; m.qgroups = a.qgroups; m.qvw = P->qvw;
   m.num_ranges = a.num_ranges; m.range_sub = a.range_sub; m.min_tokens = a.min_tokens;
   m.stream_combined = (pt == 0 && !P->mfma) ? 1 : 0;
+  m.lanes = a.lanes;
   return KVQ_OK;
 }
 

@@ -57,6 +57,7 @@ struct PartialArgs {
   int32_t range_sub;        // stream: partial slots per (unit, range): the waves sharing a range
   int32_t min_tokens;       // stream: fewest tokens per working range
   int32_t len_cap;          // min(max_len, max_blocks * BS): lengths are clamped to [0, len_cap]
+  int32_t lanes;            // vector stream: query groups of a KV head worked side by side (1, 2, 4)
 };
 
 struct MergeArgs {
@@ -68,6 +69,7 @@ struct MergeArgs {
   int32_t len_cap;          // min(max_len, max_blocks * BS): lengths are clamped to [0, len_cap]
   int32_t batch, HK, qgroups, qvw, num_ranges, range_sub, min_tokens;   // stream (part_tokens == 0)
   int32_t stream_combined;  // stream: a range's waves combined their partials of its last unit
+  int32_t lanes;            // stream: query groups side by side per set (partial slots interleave)
 };
 
 // words per block of the vector engine's q copy: 16 bf16 pairs of one query vector, then (last

@@ -12,10 +12,11 @@
 // o) (the weights are rescaled when the max moves), and the S streams' states are combined in
 // LDS the same way.
 // Output is bf16 (round to nearest even) or f32.
-// Stream schedule: the stream of T tokens is cut into R = min(num_ranges, ceil(T / min_tokens))
-// ranges; a unit's partials sit in range_sub consecutive slots per range it meets, from slot
-// (unit + first range) * range_sub on -- or (stream_combined) in the first of them only, for
-// every range whose end lies inside the unit (its waves combined their partials).
+// Stream schedule: the stream of T set positions (a set: `lanes` consecutive query groups of one KV
+// head, worked side by side) is cut into R = min(num_ranges, ceil(T / min_tokens)) ranges; per
+// range it meets, a group owns range_sub consecutive slots from ((set + range) * lanes + lane) *
+// range_sub on -- or (stream_combined) the first of them only, for every range whose end lies
+// inside the set (its waves combined their partials).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -40,6 +41,7 @@ __global__ void __launch_bounds__(NT) merge_kernel(MergeArgs a) {
   // ranges before the last one the unit meets hold one partial each and so may the last one
   int nparts = 0, nr = 0;
   int64_t mbase = 0, obase = 0, mstride = 2, ostride = a.D, slot0 = 0, slot_last = 0;
+  int64_t rstride = 0;                                          // stream: slots between ranges
   bool by_slot = false;
   if (a.part_tokens > 0) {
     nparts = len > 0 ? min((len + a.part_tokens - 1) / a.part_tokens, a.num_parts) : 0;
@@ -58,29 +60,34 @@ __global__ void __launch_bounds__(NT) merge_kernel(MergeArgs a) {
       pre += __shfl_xor(pre, off, 64);
       tot += __shfl_xor(tot, off, 64);
     }
-    const int HQG = a.HK * a.qgroups;
-    const int64_t T = (int64_t)tot * HQG;
+    // sets: L = a.lanes consecutive query groups of one KV head, worked side by side (one
+    // workgroup each) on one range
+    const int L = a.lanes, QGB = a.qgroups / L, HS = a.HK * QGB;
+    const int64_t T = (int64_t)tot * HS;
     const int64_t weff = min<int64_t>((int64_t)a.num_ranges, (T + a.min_tokens - 1) / a.min_tokens);
     const int REP = a.HQ / a.HK;
     const int hk = h / REP;
     const int jj = (h - hk * REP) * a.N + i;
     const int qg = jj / a.qvw, j = jj - qg * a.qvw;
-    const int64_t u = (int64_t)b * HQG + hk * a.qgroups + qg;
+    const int sq = hk * QGB + qg / L;                            // set within the sequence
+    const int ln = qg - (qg / L) * L;                            // the group's lane in its set
+    rstride = (int64_t)L * a.range_sub;                          // slots between a lane's ranges
+    const int64_t u = (int64_t)b * HS + sq;
     if (len > 0 && weff > 0) {
-      const int64_t start = (int64_t)pre * HQG + (int64_t)(hk * a.qgroups + qg) * len;
+      const int64_t start = (int64_t)pre * HS + (int64_t)sq * len;
       const int64_t end = start + len;
       const int64_t w_first = start * weff / T, w_last = (end - 1) * weff / T;
       if (a.stream_combined) {
-        // a range whose end lies inside the unit combined its waves' partials into one (every
-        // range before the last; the last too if it ends where the unit ends)
+        // a range whose end lies inside the set combined each lane's partials into one (every
+        // range before the last; the last too if it ends where the set ends)
         const int64_t x1_last = ((w_last + 1) * T + weff - 1) / weff;
         nr = (int)(w_last - w_first);
         nparts = nr + (x1_last == end ? 1 : a.range_sub);
       } else {
         nparts = (int)(w_last - w_first + 1) * a.range_sub;
       }
-      slot0 = (u + w_first) * a.range_sub;
-      slot_last = (u + w_last) * a.range_sub;
+      slot0 = ((u + w_first) * L + ln) * a.range_sub;
+      slot_last = ((u + w_last) * L + ln) * a.range_sub;
       by_slot = true;
       mbase = j * 2;
       obase = (int64_t)j * a.D;
@@ -101,8 +108,12 @@ __global__ void __launch_bounds__(NT) merge_kernel(MergeArgs a) {
     for (int p = sidx; p < nparts; p += S) {
       int64_t q = p;                                           // slot (stream) or partition
       if (by_slot) {
-        if (!a.stream_combined) q = slot0 + p;
-        else q = p < nr ? slot0 + (int64_t)p * a.range_sub : slot_last + (p - nr);
+        if (!a.stream_combined) {
+          const int r = p / a.range_sub;
+          q = slot0 + r * rstride + (p - r * a.range_sub);
+        } else {
+          q = p < nr ? slot0 + p * rstride : slot_last + (p - nr);
+        }
       }
       const float2 ml = *reinterpret_cast<const float2*>(mb + q * mstride);
       const float4 o = *reinterpret_cast<const float4*>(ob + q * ostride);

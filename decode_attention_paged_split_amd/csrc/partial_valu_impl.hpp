@@ -43,17 +43,21 @@
 // Two schedules share this tile engine:
 //  * fixed partitions (partition_tokens > 0): workgroup = (partition, KV head x query group,
 //    sequence); its 4 waves interleave tiles and combine in LDS; one partial per partition.
-//  * balanced stream (partition_tokens == 0): every cached token of every (sequence, KV
-//    head, query group) unit is laid end to end in one stream of T tokens, cut into R equal
-//    ranges (R = min(compute units, ceil(T / 512))), one per workgroup of 8 waves (one
-//    workgroup per compute unit).  The waves share the range's 64-token tiles through an LDS
-//    counter: the two waves on a SIMD do not progress at the same rate (the older one has
-//    issue priority), and a static split would leave the slower one running alone at the
-//    end.  Each wave writes one partial per unit that ends inside its range, at slot
-//    (unit + r) * 8 + wave (distinct for every (unit, range, wave) because ranges are contiguous
-//    and ordered); for the range's last unit the 8 waves' partials are combined in LDS first and
-//    written once, at slot (unit + r) * 8.  (A combine at every unit's end would need a barrier
-//    there, and the waves that took one tile fewer of the unit would wait a whole tile.)
+//  * balanced stream (partition_tokens == 0): a set is L consecutive query groups of one KV
+//    head of one sequence (L = 4 when a KV head's groups come in fours, 2 in pairs, else 1).
+//    Every cached token of every set is laid end to end in one stream of T positions, cut into
+//    R equal ranges (R = min(compute units / L, ceil(T / 512))); each range is worked by L
+//    workgroups of 8 waves, one per group of the set (one workgroup per compute unit), placed on
+//    one XCD so that the K/V rows one of them fetches are found in that XCD's L2 by the others,
+//    which walk the same tiles at about the same pace.  A workgroup's waves share its range's
+//    64-token tiles through an LDS counter: the two waves on a SIMD do not progress at the same
+//    rate (the older one has issue priority), and a static split would leave the slower one
+//    running alone at the end.  Each wave writes one partial per set that ends inside its range,
+//    at slot ((set + r) * L + lane) * 8 + wave (distinct for every (set, range, lane, wave)
+//    because ranges are contiguous and ordered); for the range's last set the 8 waves' partials
+//    are combined in LDS first and written once, at slot ((set + r) * L + lane) * 8.  (A combine
+//    at every set's end would need a barrier there, and the waves that took one tile fewer of the
+//    set would wait a whole tile.)
 #pragma once
 
 #include "append_rows.hpp"
@@ -836,9 +840,7 @@ template <int BITS, int D, int DV, int QVW, int GS>
 __global__ void __launch_bounds__(VALU_STREAM_WAVES * 64, 1)
 partial_stream_kernel(PartialArgs a) {
   constexpr int NW = VALU_STREAM_WAVES;
-  // the waves' tile scratch; between units (after a barrier) the waves' partials of the unit
-  // just finished, for the combine
-  // the waves' tile scratch; a wave done with the range's last unit puts its partial of it in its
+  // the waves' tile scratch; a wave done with the range's last set puts its partial of it in its
   // own scratch for the combine: [QVW][DV] o, then [QVW] m, then [QVW] l
   __shared__ __align__(16) WaveScratch<BITS, DV, QVW, GS> ws[NW];
   static_assert(sizeof(WaveScratch<BITS, DV, QVW, GS>) >= (QVW * DV + 2 * QVW) * sizeof(float),
@@ -847,10 +849,30 @@ partial_stream_kernel(PartialArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = blockIdx.x;                                      // this workgroup's range
-  const int B = a.batch, HQG = a.HK * a.qgroups;
+  const int B = a.batch;
+  // Lanes: the L query groups of a set (KV head, L consecutive groups) run side by side on L
+  // workgroups, one group each, over the same range of the set stream, so each K/V row comes from
+  // memory once for the set and the other lanes find it in the L2 cache.  Workgroups are handed
+  // to the 8 XCDs (each with its own L2) in turn by index, so the L workgroups of a range are
+  // taken 8 apart: index i runs on XCD i mod 8, and the ranges of one XCD are consecutive.
+  // L = 1: one workgroup per range, every group in turn.
+  const int L = a.lanes;
+  int g, ln;                                                     // this workgroup's range, lane
+  {
+    const int i = blockIdx.x, nwg = gridDim.x;
+    if (L > 1 && nwg % (8 * L) == 0) {
+      const int q = i >> 3;
+      ln = q % L;
+      g = (i & 7) * (nwg / (8 * L)) + q / L;
+    } else {
+      ln = i % L;
+      g = i / L;
+    }
+  }
+  const int QGB = a.qgroups / L, HS = a.HK * QGB;                // sets per KV head, per sequence
 
-  // total stream length T and the number of working ranges (every wave computes the same)
+  // total stream length T (set positions) and the number of working ranges (every wave computes
+  // the same)
   int64_t tot = 0;
   for (int c = 0; c < B; c += 64) {
     const int bb = c + lane;
@@ -859,7 +881,7 @@ partial_stream_kernel(PartialArgs a) {
     for (int off = 32; off >= 1; off /= 2) s += __shfl_xor(s, off, 64);
     tot += s;
   }
-  const int64_t T = uni64(tot) * HQG;
+  const int64_t T = uni64(tot) * HS;
   const int R = (int)min<int64_t>((int64_t)a.num_ranges, (T + a.min_tokens - 1) / a.min_tokens);
   if (g >= R) return;                                            // whole workgroup
   const int64_t x0 = ((int64_t)g * T + R - 1) / R;
@@ -877,7 +899,7 @@ partial_stream_kernel(PartialArgs a) {
       const int bb = c + lane;
       const int lv = bb < B ? clamp_len(a, bb) : 0;
       const int incl = wave_incl_scan(lv, lane);
-      const uint64_t hit = __ballot((base + incl) * HQG > x0 && lv > 0);
+      const uint64_t hit = __ballot((base + incl) * HS > x0 && lv > 0);
       if (hit) {
         const int k = __builtin_ctzll(hit);
         b = uni(c + k);
@@ -889,23 +911,24 @@ partial_stream_kernel(PartialArgs a) {
   }
   if (b < 0) return;                                             // x0 < T: not reached
   int len = uni(clamp_len(a, b));
-  const int64_t rem = x0 - pb * HQG;
-  int uu = uni((int)(rem / len));                                // unit within the sequence
+  const int64_t rem = x0 - pb * HS;
+  int uu = uni((int)(rem / len));                                // set within the sequence
   int t_lo = uni((int)(rem - (int64_t)uu * len));
 
-  // The range is a list of tiles: unit by unit, the unit's part of the range cut into 64-token
+  // The range is a list of tiles: set by set, the set's part of the range cut into 64-token
   // tiles.  The workgroup's waves take tiles from one LDS counter, so faster waves take more of
-  // them; every wave walks every unit of the range.  For a unit that ends inside the range each
-  // wave writes its own partial (possibly empty) at slot (unit + range) * NW + wave; the range's
-  // last unit, whose tiles end with the range, has its waves' partials combined in LDS and written
-  // once, at slot (unit + range) * NW (a barrier there costs nothing: every wave is done).
+  // them; every wave walks every set of the range.  For a set that ends inside the range each
+  // wave writes its own partial (possibly empty) at slot ((set + range) * L + lane) * NW + wave;
+  // the range's last set, whose tiles end with the range, has its waves' partials combined in LDS
+  // and written once, at slot ((set + range) * L + lane) * NW (a barrier there costs nothing:
+  // every wave is done).
   auto take = [&]() {
     int k = 0;
     if (lane == 0) k = atomicAdd(&tile_ctr, 1);
     return k;                                                    // valid in lane 0
   };
   int kq = uni(take());                                          // next tile this wave takes
-  int kbase = 0;                                                 // first tile of the current unit
+  int kbase = 0;                                                 // first tile of the current set
   float* const opart = a.opart;
   float* const ml = a.ml;
   int64_t x = x0;
@@ -913,8 +936,8 @@ partial_stream_kernel(PartialArgs a) {
     const int seg = (int)min<int64_t>((int64_t)(len - t_lo), x1 - x);
     const int t_end = t_lo + seg, ntiles = (seg + PV_TILE - 1) / PV_TILE;
     Unit un;
-    un.b = b; un.hk = uu / a.qgroups; un.qg = uu - un.hk * a.qgroups; un.len = len;
-    un.u = (int64_t)b * HQG + uu;
+    un.b = b; un.hk = uu / QGB; un.qg = (uu - un.hk * QGB) * L + ln; un.len = len;
+    un.u = ((int64_t)b * a.HK + un.hk) * a.qgroups + un.qg;
     Acc<BITS, DV, QVW, GS> st;
     acc_init(st);
     const int t0u = t_lo, kb = kbase;
@@ -922,16 +945,16 @@ partial_stream_kernel(PartialArgs a) {
         a, un, t_end,
         [&]() {
           const int k = uni(kq);
-          if (k - kb >= ntiles) return t_end;                    // the unit's tiles are all taken
+          if (k - kb >= ntiles) return t_end;                    // the set's tiles are all taken
           kq = take();
           return t0u + (k - kb) * PV_TILE;
         },
         ws[wave], st, lane);
     kq = uni(kq);
-    const int64_t slot = (un.u + g) * NW;
+    const int64_t slot = (((int64_t)b * HS + uu + g) * L + ln) * NW;
     if (x + seg < x1) {
-      // a unit that ends inside the range: one partial per wave (no barrier: the waves that are
-      // done with its tiles go on to the next unit)
+      // a set that ends inside the range: one partial per wave (no barrier: the waves that are
+      // done with its tiles go on to the next set)
       acc_write<BITS, DV, QVW, GS>(
           st, lane, [&](int j) { return opart + ((slot + wave) * QVW + j) * DV; },
           [&](int j, float m, float l) {
@@ -942,7 +965,7 @@ partial_stream_kernel(PartialArgs a) {
       t_lo += seg;
       if (t_lo >= len) {
         t_lo = 0;
-        if (++uu == HQG) {
+        if (++uu == HS) {
           uu = 0;
           do { ++b; } while (b < B && clamp_len(a, b) == 0);
           if (b >= B) break;                                     // (x1 <= T: not reached)
@@ -951,8 +974,8 @@ partial_stream_kernel(PartialArgs a) {
       }
       continue;
     }
-    // the range's last unit: each wave, done with its tiles, puts its partial in its own scratch;
-    // once all are there they combine (log-sum-exp) into one, written at the unit's first slot of
+    // the range's last set: each wave, done with its tiles, puts its partial in its own scratch;
+    // once all are there they combine (log-sum-exp) into one, written at the set's first slot of
     // the range
     {
       float* mine = reinterpret_cast<float*>(&ws[wave]);
@@ -995,7 +1018,7 @@ static hipError_t launch_valu(const PartialArgs& a, int B, bool q_ready, hipStre
     dim3 grid((unsigned)a.num_parts, (unsigned)(a.HK * a.qgroups), (unsigned)B);
     hipLaunchKernelGGL((partial_part_kernel<BITS, D, DV, QVW, GS>), grid, dim3(PV_WAVES * 64), 0, s, a);
   } else {
-    hipLaunchKernelGGL((partial_stream_kernel<BITS, D, DV, QVW, GS>), dim3((unsigned)a.num_ranges),
+    hipLaunchKernelGGL((partial_stream_kernel<BITS, D, DV, QVW, GS>), dim3((unsigned)(a.num_ranges * a.lanes)),
                        dim3(VALU_STREAM_WAVES * 64), 0, s, a);
   }
   return hipGetLastError();
