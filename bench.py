@@ -327,6 +327,10 @@ def main():
                          "known-size kernel that calibrates the HBM byte counters)")
     ap.add_argument("--probe-read", type=int, default=0, metavar="BYTES",
                     help="instead: time a streaming read of BYTES (achievable read bandwidth)")
+    ap.add_argument("--probe-pool", action="store_true",
+                    help="instead: time the pool-read probe over the workload's filled pool (both load patterns)")
+    ap.add_argument("--probe-sweep", action="store_true",
+                    help="with --probe-read: every launch shape of the probe (loads in flight, non-temporal, workgroups per CU)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -345,22 +349,29 @@ def main():
     torch.cuda.set_device(dev)
 
     if args.probe_read:
-        # achievable streaming-read rate: the library's read probe over BYTES (every byte read once)
+        # achievable streaming-read rate: the library's read probe over BYTES (every byte read once),
+        # at the default launch shape or (--probe-sweep) over loads in flight, non-temporal loads
+        # and workgroups per compute unit; one JSON line per shape
         buf = torch.ones(args.probe_read // 4, dtype=torch.float32, device=dev)
         sink = torch.zeros(1, dtype=torch.int32, device=dev)
-        for _ in range(3):
-            kvq.kvq_probe_read(buf, sink)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
-            kvq.kvq_probe_read(buf, sink)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
-        print(json.dumps({"probe": "read (kvq_probe_read)", "bytes_read": buf.numel() * 4,
-                          "us_per_read": round(ms * 1e3, 2),
-                          "GB_per_s": round(buf.numel() * 4 / (ms * 1e-3) / 1e9, 1)}))
+        shapes = [(4, False, 32)]
+        if args.probe_sweep:
+            shapes = [(u, nt, bpc) for nt in (False, True) for u in (1, 2, 4, 8, 16) for bpc in (4, 8, 16, 32)]
+        for u, nt, bpc in shapes:
+            for _ in range(3):
+                kvq.kvq_probe_read_ex(buf, sink, u, nt, bpc)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(args.steps):
+                kvq.kvq_probe_read_ex(buf, sink, u, nt, bpc)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            print(json.dumps({"probe": "read (kvq_probe_read_ex)", "loads_in_flight": u, "nontemporal": nt,
+                              "blocks_per_cu": bpc, "bytes_read": buf.numel() * 4,
+                              "us_per_read": round(ms * 1e3, 2),
+                              "GB_per_s": round(buf.numel() * 4 / (ms * 1e-3) / 1e9, 1)}), flush=True)
         return
 
     if args.probe_copy:
@@ -386,6 +397,28 @@ def main():
     flush = None if args.no_cold else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     engines = {"auto": kvq.ENGINE_AUTO, "vector": kvq.ENGINE_VECTOR, "matrix": kvq.ENGINE_MATRIX}
     bench = Bench(kvq, torch, w, dev)
+    if args.probe_pool:
+        # the pool-read probe over this workload's pool: every cached row's K/V codes and scales
+        # read through the block table, no arithmetic; one token per lane and coalesced
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        eff = w.effective_bytes()
+        for coalesced in (False, True):
+            for _ in range(3):
+                kvq.kvq_probe_pool_read(bench.pool, bench.table, bench.lengths, w.max_len, coalesced, sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(args.steps):
+                kvq.kvq_probe_pool_read(bench.pool, bench.table, bench.lengths, w.max_len, coalesced, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            print(json.dumps({"probe": "pool read (kvq_probe_pool_read)", "workload": w.name,
+                              "pattern": "coalesced" if coalesced else "token per lane", "bytes_read": eff,
+                              "us_per_read": round(ms * 1e3, 2), "GB_per_s": round(eff / (ms * 1e-3) / 1e9, 1)}),
+                  flush=True)
+        bench.close()
+        return
     head = bench.measure(engines[args.engine], args.steps, args.warmup, args.partition_tokens,
                          flush=flush, label=f"{w.name} ({args.engine} engine)")
     t = head.pop("_t")

@@ -29,7 +29,7 @@ __all__ = [
     "paged_decode_partition_tokens", "paged_decode_attention", "paged_decode_partial",
     "paged_decode_merge", "paged_decode_step", "paged_decode_step_partial", "paged_decode_step_noalloc",
     "NOALLOC_WORKSPACE_BYTES", "kv_gather_debug", "make_shape", "gather", "decode_step",
-    "kvq_timing_enable", "kvq_timing_read", "kvq_probe_read", "TIMING_PREP", "TIMING_PARTIAL", "TIMING_MERGE", "PARTITION_AUTO", "PARTITION_STREAM",
+    "kvq_timing_enable", "kvq_timing_read", "kvq_probe_read", "kvq_probe_read_ex", "kvq_probe_pool_read", "TIMING_PREP", "TIMING_PARTIAL", "TIMING_MERGE", "PARTITION_AUTO", "PARTITION_STREAM",
     "PLANES", "LIB_PATH",
 ]
 
@@ -109,6 +109,10 @@ def lib() -> ctypes.CDLL:
             "kv_gather_debug": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                _P * 6, _P]),
             "kvq_probe_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
+            "kvq_probe_read_ex": (ctypes.c_int, [_P, ctypes.c_size_t, _P, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_int32, _P]),
+            "kvq_probe_pool_read": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.c_int32, _P, _P]),
             "kvq_timing_enable": (ctypes.c_int, [ctypes.c_int32]),
             "kvq_timing_read": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
                                                ctypes.POINTER(ctypes.c_int32)]),
@@ -155,6 +159,23 @@ def kvq_probe_read(buf, sink, stream=None) -> None:
     """Enqueue the streaming-read probe over the device tensor buf (sink: a device int32 tensor)."""
     _need_cuda(buf, sink)
     _check(lib().kvq_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+
+
+def kvq_probe_pool_read(pool, block_table, lengths, max_len, coalesced=False, sink=None, stream=None) -> None:
+    """Enqueue the pool-read probe over every cached row of the batch (block_table [B, max_blocks]
+    and lengths [B] int32 device tensors; sink a device int32 tensor)."""
+    _need_cuda(block_table, lengths, sink)
+    B, mb = block_table.shape
+    _check(lib().kvq_probe_pool_read(pool.handle, _ptr(block_table), _ptr(lengths), int(B), int(mb), int(max_len),
+                                     1 if coalesced else 0, _ptr(sink), _stream(stream)))
+
+
+def kvq_probe_read_ex(buf, sink, loads_in_flight=4, nontemporal=False, blocks_per_cu=32, stream=None) -> None:
+    """The streaming-read probe with its launch shape chosen (loads in flight per thread,
+    non-temporal loads, workgroups per compute unit)."""
+    _need_cuda(buf, sink)
+    _check(lib().kvq_probe_read_ex(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(loads_in_flight),
+                                   1 if nontemporal else 0, int(blocks_per_cu), _stream(stream)))
 
 
 def kvq_timing_read(kind: int):

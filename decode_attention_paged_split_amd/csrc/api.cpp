@@ -348,12 +348,57 @@ int kvq_timing_read(int32_t kind, double* avg_ms, int32_t* count) {
   return KVQ_OK;
 }
 
-int kvq_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+int kvq_probe_read_ex(const void* buf, size_t bytes, uint32_t* sink, int32_t loads_in_flight, int32_t nontemporal,
+                      int32_t blocks_per_cu, void* stream) {
   if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4))
     return fail(KVQ_ERR_INVALID, "kvq_probe_read: buf (16-byte aligned) and sink must be device pointers");
   if (bytes == 0 || bytes % 16 != 0) return fail(KVQ_ERR_INVALID, "kvq_probe_read: bytes must be a positive multiple of 16");
-  hipError_t e = kvq::launch_probe_read(buf, bytes, sink, 32 * device_cus(), static_cast<hipStream_t>(stream));
+  const int u = loads_in_flight;
+  if (!(u == 1 || u == 2 || u == 4 || u == 8 || u == 16))
+    return fail(KVQ_ERR_INVALID, "kvq_probe_read_ex: loads_in_flight must be 1, 2, 4, 8 or 16, got %d", u);
+  if (blocks_per_cu < 1 || blocks_per_cu > 64)
+    return fail(KVQ_ERR_INVALID, "kvq_probe_read_ex: blocks_per_cu must be 1..64, got %d", blocks_per_cu);
+  hipError_t e = kvq::launch_probe_read(buf, bytes, sink, blocks_per_cu * device_cus(), u, nontemporal != 0,
+                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return KVQ_OK;
+}
+
+int kvq_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  return kvq_probe_read_ex(buf, bytes, sink, 4, 0, 32, stream);
+}
+
+int kvq_probe_pool_read(const kvq_pool* pool, const int32_t* block_table, const int32_t* lengths, int32_t batch,
+                        int32_t max_blocks_per_seq, int32_t max_len, int32_t coalesced, uint32_t* sink,
+                        void* stream) {
+  if (!pool) return fail(KVQ_ERR_INVALID, "pool is NULL");
+  if (!block_table || !lengths || !sink || !aligned(block_table, 4) || !aligned(lengths, 4) || !aligned(sink, 4))
+    return fail(KVQ_ERR_INVALID, "kvq_probe_pool_read: block_table, lengths and sink must be device pointers");
+  if (batch < 1 || max_blocks_per_seq < 1 || max_len < 1 || batch > 65535)
+    return fail(KVQ_ERR_INVALID, "kvq_probe_pool_read: batch (1..65535), max_blocks_per_seq and max_len must be positive");
+  const kvq_pool_desc& d = pool->desc;
+  kvq::PoolProbeArgs a{};
+  a.krow = (int)plane_row_bytes(&d, KVQ_PLANE_K);
+  a.vrow = (int)plane_row_bytes(&d, KVQ_PLANE_V);
+  {
+    const int kc = a.krow / 16;
+    if (a.krow != a.vrow || a.krow % 16 != 0 || !(kc == 2 || kc == 4 || kc == 6 || kc == 8 || kc == 16 || kc == 32))
+      return fail(KVQ_ERR_UNSUPPORTED,
+                  "kvq_probe_pool_read: K and V rows must be equal and 32, 64, 96, 128, 256 or 512 bytes (%d, %d)",
+                  a.krow, a.vrow);
+  }
+  a.k = static_cast<const uint8_t*>(pool->planes[KVQ_PLANE_K]);
+  a.v = static_cast<const uint8_t*>(pool->planes[KVQ_PLANE_V]);
+  const int sp[4] = {KVQ_PLANE_K_SCALE, KVQ_PLANE_K_BIAS, KVQ_PLANE_V_SCALE, KVQ_PLANE_V_BIAS};
+  for (int p = 0; p < 4; ++p) {
+    a.sp[p] = static_cast<const uint8_t*>(pool->planes[sp[p]]);
+    a.srow[p] = a.sp[p] ? (int)plane_row_bytes(&d, sp[p]) : 0;
+  }
+  a.table = block_table; a.lengths = lengths; a.sink = sink;
+  a.HK = d.num_kv_heads; a.BS = d.block_size; a.max_blocks = max_blocks_per_seq; a.num_blocks = d.num_blocks;
+  a.len_cap = (int)std::min<long>(max_len, (long)max_blocks_per_seq * d.block_size);
+  hipError_t e = kvq::launch_probe_pool(a, batch, coalesced != 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pool probe launch");
   return KVQ_OK;
 }
 

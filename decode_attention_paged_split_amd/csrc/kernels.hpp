@@ -84,9 +84,25 @@ constexpr int Q_COPY_TAIL = 512;
 int set_error(int code, const char* msg);
 
 hipError_t launch_append(const AppendArgs& a, int bits, hipStream_t stream);
-// streaming-read probe over bytes (a multiple of 16) of buf with `blocks` workgroups of 256
-hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
+// streaming-read probe over bytes (a multiple of 16) of buf with `blocks` workgroups of 256,
+// loads_in_flight (1, 2, 4, 8 or 16) 16-byte loads per thread at a time, optionally non-temporal
+hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, int loads_in_flight,
+                             bool nontemporal, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
+
+// pool-read probe: every cached row (K, V, and the four scale planes where sp[p] is set) of every
+// (sequence, KV head), through the block table; krow and vrow multiples of 16
+struct PoolProbeArgs {
+  const uint8_t* k;
+  const uint8_t* v;
+  const uint8_t* sp[4];     // k scale, k bias, v scale, v bias planes (nullptr: none)
+  const int32_t* table;
+  const int32_t* lengths;
+  uint32_t* sink;
+  int32_t HK, BS, max_blocks, num_blocks, len_cap;
+  int32_t krow, vrow, srow[4];
+};
+hipError_t launch_probe_pool(const PoolProbeArgs& a, int B, bool coalesced, hipStream_t stream);
 
 // qvw: query vectors per workgroup (REP * N split into qgroups groups of qvw)
 // q_ready: the vector engine's q copy is already in the workspace (decode step); gs: the pool's

@@ -345,6 +345,23 @@ __device__ __forceinline__ RowPart<KCP> load_row_part(const char* plane, int row
   return r;
 }
 
+// The same part (rows of one part only) of the rows of a tile's 64 tokens, loaded coalesced: lane
+// l takes 16-byte piece l % KCP of the row of token l / KCP + c * (64 / KCP), c < KCP, so that
+// consecutive lanes read consecutive bytes of a block (a block holds its rows of one KV head
+// contiguously); row is each lane's own token's pool row.
+template <int KCP>
+__device__ __forceinline__ RowPart<KCP> load_rows_coalesced(const char* plane, int row, int rowb, int lane) {
+  static_assert(64 % KCP == 0, "whole tokens per wave load");
+  RowPart<KCP> r;
+  const int piece = lane % KCP, tok0 = lane / KCP;
+#pragma unroll
+  for (int c = 0; c < KCP; ++c) {
+    const int rr = __shfl(row, tok0 + c * (64 / KCP), 64);
+    r.c[c] = *reinterpret_cast<const u32x4*>(plane + (int64_t)rr * rowb + piece * 16);
+  }
+  return r;
+}
+
 // Tiles of unit un (tokens < t1), accumulated into st by one wave.  grab() returns the first
 // token of the next tile this wave takes (>= t1: none left), valid in lane 0 at least; it is
 // called one tile ahead and read (made uniform) only a tile later, so an atomic behind it has a
@@ -360,6 +377,13 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
   constexpr int GV = Gv::G, NPV = Gv::NP, KCPV = Gv::KCP, ROWBV = Gv::ROWB, KPBV = Gv::KPB;
   constexpr bool AFF = Gm::AFF;
   constexpr int QBS = Q_BLOCK_WORDS;                              // words per q block
+  // Rows of one part (<= 128 bytes; K no wider than V) are loaded coalesced, a tile's 64 rows as
+  // 64 * KCP pieces in token order, and reach their token's lane through LDS: V's by the staging
+  // the V phase does anyway, K's by a round trip at the top of the tile.  Wider rows, rows of 48
+  // or 96 bytes (3- and 6-bit codes at head dim 128) and rows under 64 bytes (where the K round
+  // trip costs more than it saves: 2-bit codes at head dim 128 measured 1.4 % slower) are loaded
+  // one token per lane.
+  constexpr bool COAL = NP == 1 && NPV == 1 && KPB <= KPBV && KCP >= 4 && 64 % KCP == 0 && 64 % KCPV == 0;
   int tt = uni(grab());
   if (tt >= t1) return;
   int tn_raw = grab();
@@ -396,9 +420,27 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
       load_plane_row<GV>(a.vb, row, sc.vb);
     }
   };
-  auto stage_v = [&](const RowPart<KCPV>& src) {                 // this lane's V row part -> LDS
+  auto stage_v = [&](const RowPart<KCPV>& src) {                 // V row part(s) -> LDS rows
+    if constexpr (COAL) {
+      const int piece = lane % KCPV, tok0 = lane / KCPV;
 #pragma unroll
-    for (int c = 0; c < KCPV; ++c) *reinterpret_cast<u32x4*>(&ws.v[lane][16 * c]) = src.c[c];
+      for (int c = 0; c < KCPV; ++c)
+        *reinterpret_cast<u32x4*>(&ws.v[tok0 + c * (64 / KCPV)][16 * piece]) = src.c[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < KCPV; ++c) *reinterpret_cast<u32x4*>(&ws.v[lane][16 * c]) = src.c[c];
+    }
+  };
+  auto own_k_row = [&](const RowPart<KCP>& src) {                // coalesced K pieces -> own row
+    RowPart<KCP> r;
+    const int piece = lane % KCP, tok0 = lane / KCP;
+#pragma unroll
+    for (int c = 0; c < KCP; ++c)
+      *reinterpret_cast<u32x4*>(&ws.v[tok0 + c * (64 / KCP)][16 * piece]) = src.c[c];
+    wave_lds_sync();
+#pragma unroll
+    for (int c = 0; c < KCP; ++c) r.c[c] = *reinterpret_cast<const u32x4*>(&ws.v[lane][16 * c]);
+    return r;
   };
 
   // ---- prologue: the unit's q copy into the scalar cache (eight 64-byte lines requested per wait:
@@ -427,10 +469,14 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
     }
   }
   int row = row_of(min(tt + lane, t1 - 1), table_entry(min(tt + lane, t1 - 1)));
-  RowPart<KCP> kcur = load_row_part<KCP>(kplane, row, ROWB, 0);
+  RowPart<KCP> kcur;
+  if constexpr (COAL) kcur = load_rows_coalesced<KCP>(kplane, row, ROWB, lane);
+  else kcur = load_row_part<KCP>(kplane, row, ROWB, 0);
   Scales<G, GV> sc, scn;
   load_scales(row, sc);
-  RowPart<KCPV> vcur = load_row_part<KCPV>(vplane, row, ROWBV, 0);
+  RowPart<KCPV> vcur;
+  if constexpr (COAL) vcur = load_rows_coalesced<KCPV>(vplane, row, ROWBV, lane);
+  else vcur = load_row_part<KCPV>(vplane, row, ROWBV, 0);
 
   while (true) {
     const int tn = uni(tn_raw);
@@ -458,7 +504,9 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
       for (int p = 0; p < 17; ++p) dst[p] = qt[b * QBS + p];
     };
     q_fetch(0, qb[0]);
-    RowPart<KCP> kpart = kcur;
+    RowPart<KCP> kpart;
+    if constexpr (COAL) kpart = own_k_row(kcur);
+    else kpart = kcur;
 #pragma unroll
     for (int h = 0; h < NP; ++h) {
       RowPart<KCP> knext;
@@ -518,9 +566,11 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
     const int row_next = has_next ? row_of(t_next, tbl_next) : row;
     constexpr bool RELOAD = BITS == 4 && D == 256 && DV == 256 && QVW == 8;
     if (RELOAD || has_next) {
-      kcur = load_row_part<KCP>(kplane, row_next, ROWB, 0);
+      if constexpr (COAL) kcur = load_rows_coalesced<KCP>(kplane, row_next, ROWB, lane);
+      else kcur = load_row_part<KCP>(kplane, row_next, ROWB, 0);
       load_scales(row_next, scn);
-      vcur = load_row_part<KCPV>(vplane, row_next, ROWBV, 0);
+      if constexpr (COAL) vcur = load_rows_coalesced<KCPV>(vplane, row_next, ROWBV, lane);
+      else vcur = load_row_part<KCPV>(vplane, row_next, ROWBV, 0);
     }
 
     // ---- softmax, one token per lane

@@ -1,31 +1,144 @@
-// Streaming-read probe: the achievable HBM read rate on this device, the reference beside which
-// the partial kernel's effective K/V bandwidth is reported.  Every 16-byte chunk of the buffer is
-// loaded once (grid-stride, four loads in flight per thread); the loaded words are folded into
-// one value per thread that is stored only if it equals a constant no buffer here produces, so the
-// loads stay and nothing is written.
+// Read probes, measurement aids: the achievable HBM read rate on this device, the reference beside
+// which the partial kernel's effective K/V bandwidth is reported.
+//  * Streaming read: every 16-byte chunk of a buffer is loaded once (grid-stride, U loads in
+//    flight per thread, optionally non-temporal).
+//  * Pool read: every cached row of a paged pool (K and V codes or values, scales and biases),
+//    reached through the block table as the partial kernel reaches it, with no arithmetic: either
+//    one token per lane (lane l loads its token's row in 16-byte pieces, the partial kernel's
+//    pattern) or coalesced (consecutive lanes load consecutive 16-byte pieces of the rows a block
+//    holds contiguously for one KV head).  The rate of the two against the streaming read tells
+//    what the paged layout and the load pattern cost.
+// The loaded words are folded into one value per thread that is stored only if it equals a
+// constant no buffer here produces, so the loads stay and nothing is written.
 #include "kernels.hpp"
 
 namespace kvq {
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int U, bool NT>
+__device__ __forceinline__ uint4 probe_load(const uint4* p) {
+  if constexpr (NT) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *p;
+  }
+}
+
+template <int U, bool NT>
 __global__ void __launch_bounds__(256) probe_read_kernel(const uint4* __restrict__ p, size_t n16, uint32_t* sink) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = probe_load<U, NT>(p + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n16; i += stride) {
-    const uint4 a = p[i];
+    const uint4 a = probe_load<U, NT>(p + i);
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
-hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t s) {
-  hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                     static_cast<const uint4*>(buf), bytes / 16, sink);
+template <int U>
+static hipError_t launch_probe_u(const uint4* p, size_t n16, uint32_t* sink, int blocks, bool nt, hipStream_t s) {
+  if (nt) hipLaunchKernelGGL((probe_read_kernel<U, true>), dim3((unsigned)blocks), dim3(256), 0, s, p, n16, sink);
+  else hipLaunchKernelGGL((probe_read_kernel<U, false>), dim3((unsigned)blocks), dim3(256), 0, s, p, n16, sink);
   return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, int loads_in_flight,
+                             bool nontemporal, hipStream_t s) {
+  const uint4* p = static_cast<const uint4*>(buf);
+  const size_t n16 = bytes / 16;
+  switch (loads_in_flight) {
+    case 1: return launch_probe_u<1>(p, n16, sink, blocks, nontemporal, s);
+    case 2: return launch_probe_u<2>(p, n16, sink, blocks, nontemporal, s);
+    case 4: return launch_probe_u<4>(p, n16, sink, blocks, nontemporal, s);
+    case 8: return launch_probe_u<8>(p, n16, sink, blocks, nontemporal, s);
+    case 16: return launch_probe_u<16>(p, n16, sink, blocks, nontemporal, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// One wave per 64-token tile of one (sequence, KV head): grid (tiles / 4, HK, B), 256 threads.
+// Both patterns issue the same loads per lane, all before any is used: KC 16-byte pieces of K and
+// KC of V (KC = the row's pieces; a tile's rows are 64 * KC pieces).  Token per lane: lane l
+// loads pieces 0..KC-1 of token l's row.  Coalesced: lane l loads pieces l, l + 64, ... of the
+// tile's rows taken in token order, so consecutive lanes read consecutive bytes of a block.
+template <int KC, bool COALESCED>
+__global__ void __launch_bounds__(256) probe_pool_kernel(PoolProbeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+  const int hk = blockIdx.y, b = blockIdx.z;
+  const int len = max(0, min(a.lengths[b], a.len_cap));
+  if (t0 >= len) return;
+  const int nt = min(64, len - t0);
+  const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
+  auto prow = [&](int t) -> int64_t {                            // pool row of token t
+    const int phys = min(max(trow[t / a.BS], 0), a.num_blocks - 1);
+    return ((int64_t)phys * a.HK + hk) * a.BS + t % a.BS;
+  };
+  const uint4* kp = reinterpret_cast<const uint4*>(a.k);
+  const uint4* vp = reinterpret_cast<const uint4*>(a.v);
+  uint4 kv[KC], vv[KC];
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    int tok, piece;
+    if constexpr (COALESCED) {
+      const int j = lane + 64 * i;
+      tok = j / KC;
+      piece = j - tok * KC;
+    } else {
+      tok = lane;
+      piece = i;
+    }
+    tok = min(tok, nt - 1);                                      // past the end: the last row again
+    const int64_t r = prow(t0 + tok);
+    kv[i] = kp[r * KC + piece];
+    vv[i] = vp[r * KC + piece];
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < KC; ++i) acc ^= kv[i].x ^ kv[i].y ^ kv[i].z ^ kv[i].w ^ vv[i].x ^ vv[i].y ^ vv[i].z ^ vv[i].w;
+  // scale and bias rows (2-byte units), token per lane either way
+  if (lane < nt) {
+    const int64_t r = prow(t0 + lane);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if (!a.sp[p]) continue;
+      const uint16_t* sp = reinterpret_cast<const uint16_t*>(a.sp[p] + r * a.srow[p]);
+      for (int c = 0; c < a.srow[p] / 2; ++c) acc ^= sp[c];
+    }
+  }
+  if (acc == 0x9E3779B9u) a.sink[0] = acc;
+}
+
+template <int KC>
+static hipError_t launch_probe_pool_kc(const PoolProbeArgs& a, dim3 grid, bool coalesced, hipStream_t s) {
+  if (coalesced) hipLaunchKernelGGL((probe_pool_kernel<KC, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((probe_pool_kernel<KC, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_pool(const PoolProbeArgs& a, int B, bool coalesced, hipStream_t s) {
+  const int tiles = (a.len_cap + 63) / 64;
+  const dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)a.HK, (unsigned)B);
+  if (a.krow != a.vrow) return hipErrorInvalidValue;
+  switch (a.krow / 16) {
+    case 2: return launch_probe_pool_kc<2>(a, grid, coalesced, s);
+    case 4: return launch_probe_pool_kc<4>(a, grid, coalesced, s);
+    case 6: return launch_probe_pool_kc<6>(a, grid, coalesced, s);
+    case 8: return launch_probe_pool_kc<8>(a, grid, coalesced, s);
+    case 16: return launch_probe_pool_kc<16>(a, grid, coalesced, s);
+    case 32: return launch_probe_pool_kc<32>(a, grid, coalesced, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace kvq

@@ -293,6 +293,28 @@ int kvq_timing_read(int32_t kind, double* avg_ms, int32_t* count);
  * (events around the call).  Errors: KVQ_ERR_INVALID for NULL or misaligned pointers or a bad
  * size. */
 int kvq_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+/* The same probe with its launch shape chosen: loads_in_flight 16-byte loads per thread at a time
+ * (1, 2, 4, 8 or 16), non-temporal loads when nontemporal != 0, blocks_per_cu workgroups of 256
+ * threads per compute unit (1..64); kvq_probe_read is (4, 0, 32).  For finding the device's
+ * streaming-read ceiling.  Errors: as kvq_probe_read, and KVQ_ERR_INVALID for a value outside
+ * those sets. */
+int kvq_probe_read_ex(const void* buf, size_t bytes, uint32_t* sink, int32_t loads_in_flight, int32_t nontemporal,
+                      int32_t blocks_per_cu, void* stream);
+
+/* Pool-read probe, a measurement aid: enqueues one kernel that reads every cached row of every
+ * (sequence, KV head) of the pool -- K and V codes or values and, for affine pages, the four
+ * scale and bias planes -- reached through block_table ([batch, max_blocks_per_seq] int32,
+ * device) for the tokens t < min(lengths[b], max_len, max_blocks_per_seq * block_size) (lengths:
+ * [batch] int32, device), with no arithmetic.  coalesced = 0: one token per lane, each lane
+ * loading its row in 16-byte pieces (the partial kernel's pattern); coalesced != 0: consecutive
+ * lanes load consecutive 16-byte pieces of the rows a block holds contiguously for one KV head.
+ * Either way one wave takes 64 tokens and issues all its K/V loads before using any.  Table
+ * entries outside the pool are clamped into it.  sink as for kvq_probe_read.  The caller times
+ * it.  Errors: KVQ_ERR_INVALID for NULL or misaligned pointers or non-positive sizes,
+ * KVQ_ERR_UNSUPPORTED unless K and V rows are equal and 32, 64, 96, 128, 256 or 512 bytes. */
+int kvq_probe_pool_read(const kvq_pool* pool, const int32_t* block_table, const int32_t* lengths, int32_t batch,
+                        int32_t max_blocks_per_seq, int32_t max_len, int32_t coalesced, uint32_t* sink,
+                        void* stream);
 
 /* Message for the calling thread's last failing call ("" if none).  The pages fail with a typed
  * error that carries a message, never a silent truncation ([P134] cache.ts, PagedPoolExhausted:

@@ -57,6 +57,11 @@ def test_probe_read_rejects_bad_arguments(lib):
     assert lib.kvq_probe_read(None, 1024, None, None) == -1
     assert lib.kvq_probe_read(ctypes.c_void_p(256), 1000, ctypes.c_void_p(512), None) == -1   # not x16
     assert lib.kvq_probe_read(ctypes.c_void_p(255), 1024, ctypes.c_void_p(512), None) == -1   # misaligned
+    P = ctypes.c_void_p(256)
+    for u, bpc in ((3, 32), (0, 32), (32, 32), (4, 0), (4, 65)):
+        assert lib.kvq_probe_read_ex(P, 1024, P, u, 0, bpc, None) == -1, (u, bpc)
+        assert lib.kvq_last_error().decode()
+    assert lib.kvq_probe_pool_read(None, P, P, 1, 1, 1, 0, P, None) == -1
 
 
 def test_struct_layouts():
