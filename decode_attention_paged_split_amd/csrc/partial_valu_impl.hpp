@@ -443,10 +443,13 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
     return r;
   };
 
-  // ---- prologue: the unit's q copy into the scalar cache (eight 64-byte lines requested per wait:
-  // the K phase asks for its blocks one after the other and would wait for every line's first miss
-  // in turn; the last group may reach past the copy, into the next unit's or the workspace's
+  // ---- prologue: the first tile's block-table entries are requested, then the unit's q copy is
+  // pulled into the scalar cache while they arrive (eight 64-byte lines requested per wait: the K
+  // phase asks for its blocks one after the other and would wait for every line's first miss in
+  // turn; the last group may reach past the copy, into the next unit's or the workspace's
   // Q_COPY_TAIL bytes), then rows, K and V part 0 and scales of the first tile
+  const int t_first = min(tt + lane, t1 - 1);
+  const int tbl_first = table_entry(t_first);
   {
     constexpr int QL = (G * NHB * QVW * QBS + 15) / 16;           // 64-byte lines of the q copy
 #pragma unroll
@@ -468,7 +471,7 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
           : "=&s"(sink) : "s"(base) : "memory");
     }
   }
-  int row = row_of(min(tt + lane, t1 - 1), table_entry(min(tt + lane, t1 - 1)));
+  int row = row_of(t_first, tbl_first);
   RowPart<KCP> kcur;
   if constexpr (COAL) kcur = load_rows_coalesced<KCP>(kplane, row, ROWB, lane);
   else kcur = load_row_part<KCP>(kplane, row, ROWB, 0);
