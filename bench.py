@@ -39,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+SETTLE_S = 0.2              # seconds of untimed steps before the warm-up steps (clock ramp-up)
 # MI355X published dense fp32 vector peak (256 CUs x 4 SIMDs x 16 lanes x 2 FMA x 2 flop x 2.4 GHz:
 # packed FP32).  Code here issues no packed FP32, so the vector path's attainable ceiling is half
 # of it for its f32 FMAs (its 16-bit dot2 steps still do 2 MACs per lane-op).
@@ -248,6 +249,16 @@ class Bench:
         torch, w = self.torch, self.w
         shp, wsp = self.config(engine, partition_tokens)
         pt = self.kvq.paged_decode_partition_tokens(self.pool, shp)
+        # the GPU idles at a low clock and takes some tens of ms of load to reach its working clock
+        # (c3: 197 us/step timed after 10 warm-up steps, 180 after 300, 178 after 1000, the kernels
+        # themselves unchanged); so before the W warm-up steps, steps run for at least SETTLE_S
+        settle = 0
+        t0 = time.time()
+        while time.time() - t0 < SETTLE_S:
+            for _ in range(8):
+                self.step(shp, wsp)
+            torch.cuda.synchronize()
+            settle += 8
         for _ in range(warmup):
             self.step(shp, wsp)
         torch.cuda.synchronize()
@@ -259,7 +270,7 @@ class Bench:
                "partial_pass_us": round(float(np.mean(t["par"])) * 1e3, 2),
                "merge_us_events": round(float(np.mean(t["mer"])) * 1e3, 2),
                "kernels_us": {k: round(v * 1e3, 2) for k, v in t["kern"].items()},
-               "partition_tokens": pt, "_t": t}
+               "partition_tokens": pt, "settle_steps": settle, "_t": t}
         log(f"[bench] {label or w.name}: {t['ms'] * 1e3:.1f} us/step (events: median "
             f"{rec['step_us_events']['median']}, p10 {rec['step_us_events']['p10']}, p90 "
             f"{rec['step_us_events']['p90']}); kernels (library events): prep {t['kern']['prep'] * 1e3:.1f}, "
@@ -472,6 +483,8 @@ def main():
         "step_us_events": head["step_us_events"], "effective_bytes": eff,
         "kernels_us": head["kernels_us"], "partial_pass_us": head["partial_pass_us"],
         "merge_us_events": head["merge_us_events"],
+        "settle": {"seconds_min": SETTLE_S, "steps": head["settle_steps"],
+                   "note": "untimed steps before the W warm-up steps, until the GPU clock has left its idle level"},
         "roofline": roof,
     }
     if "cold" in head:
