@@ -20,7 +20,7 @@ the HBM time.
 Prints one JSON line (stdout, last line): effective K/V GB/s (bytes of codes + scales +
 biases of every cached token, per step) with the fraction of the 8 TB/s HBM peak,
 microseconds per step (mean of K back-to-back steps; median and p10/p90 of per-step events;
-cold steps after a 1 GiB write), the partial kernel's roofline figures, and the CPU oracle
+cold steps after a 1 GiB read), the partial kernel's roofline figures, and the CPU oracle
 timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -171,6 +171,7 @@ class Bench:
         self.table = torch.from_numpy(w.table).to(dev)
         self.lengths = torch.from_numpy(w.lengths.astype(np.int32)).to(dev)
         self.out = torch.empty((w.B, w.HQ, w.N, w.DV), dtype=torch.bfloat16, device=dev)
+        self.sink = torch.zeros(1, dtype=torch.int32, device=dev)        # the cold flush's read probe
         torch.cuda.synchronize()
         log(f"[bench] setup {time.time() - t_setup:.0f} s")
 
@@ -197,8 +198,10 @@ class Bench:
         end opens the next step) and give the per-step distribution; then nsteps under the
         library's launch timing, which brackets each kernel with events on its own stream, give
         the kernels' durations.  Event records between kernels delay the next launch by a few
-        microseconds, so each pass gives only its own figure.  Cold: the 1 GiB write, an event,
-        the step, an event, per step.  Returns a dict: ms per step, per-step / partial-pass /
+        microseconds, so each pass gives only its own figure.  Cold: a read of 1 GiB (the
+        library's streaming-read probe: it evicts the pool from the L2s and the 256 MB Infinity
+        Cache and, unlike a write, leaves no dirty lines to be written back inside the step), an
+        event, the step, an event, per step.  Returns a dict: ms per step, per-step / partial-pass /
         merge ms lists, wall s (second pass), and the mean ms of the prep, partial and merge
         kernels."""
         torch, kvq = self.torch, self.kvq
@@ -222,7 +225,7 @@ class Bench:
         ev0.record()
         for i in range(nsteps):
             if flush_buf is not None:
-                flush_buf.fill_(1)
+                kvq.kvq_probe_read(flush_buf, self.sink)
                 starts[i].record()
             self.step(shp, wsp, mids[i])
             ends[i].record()
@@ -231,7 +234,7 @@ class Bench:
         kvq.kvq_timing_enable(True)
         for _ in range(nsteps):
             if flush_buf is not None:
-                flush_buf.fill_(1)
+                kvq.kvq_probe_read(flush_buf, self.sink)
             self.step(shp, wsp)
         torch.cuda.synchronize()
         kern = {k: kvq.kvq_timing_read(v)[0] for k, v in
@@ -283,8 +286,9 @@ class Bench:
                            "partial_pass_us": round(float(np.mean(tc["par"])) * 1e3, 2),
                            "partial_kernel_us": round(tc["kern"]["partial"] * 1e3, 2),
                            "merge_us": round(float(np.mean(tc["mer"])) * 1e3, 2),
-                           "note": "1 GiB written before each step (more than the 256 MB Infinity Cache and "
-                                   "the L2s); step = event after the write to event after the merge"}
+                           "note": "1 GiB read before each step (more than the 256 MB Infinity Cache and the "
+                                   "L2s; a read leaves no dirty lines to drain inside the step); step = event "
+                                   "after the read to event after the merge"}
             log(f"[bench] {label or w.name} cold: {tc['ms'] * 1e3:.1f} us/step")
         return rec
 
@@ -328,7 +332,7 @@ def main():
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--engine", choices=["auto", "vector", "matrix"], default="auto",
                     help="partial-pass engine: vector ALU (the default) or matrix cores (4-bit pages)")
-    ap.add_argument("--no-cold", action="store_true", help="skip the cold steps (1 GiB written before each)")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold steps (1 GiB read before each)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the matrix-engine and 32k-context lines beside the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
