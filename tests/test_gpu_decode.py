@@ -50,7 +50,7 @@ def filled():
 
 
 @pytest.mark.parametrize("name", list(SMALL))
-@pytest.mark.parametrize("pt", [kvq.PARTITION_STREAM, kvq.PARTITION_AUTO, 64, 333])
+@pytest.mark.parametrize("pt", [kvq.PARTITION_STREAM, kvq.PARTITION_AUTO, 64, 333, 512])
 def test_decode_parity(filled, name, pt):
     print(f"decode {name} pt={pt}", flush=True)
     w, pool, ref = filled(name, **SMALL[name])

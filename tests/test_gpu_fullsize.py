@@ -4,7 +4,8 @@ Each workload is built at its full size (every sequence, every cached token), th
 the append kernel with every row but each sequence's last N, and one decode step run as the bench
 runs it (paged_decode_step: the step's new rows appended at the slots the block table gives them,
 the partial pass with the automatic schedule and engine, the merge; for the 4-bit head-dim-256
-workloads also the matrix-core variant).  The oracle cannot take the whole batch in seconds, so the
+workloads also the matrix-core variant, for the c4 shapes also 1, 16 and 256 fixed partitions per
+131072-token sequence).  The oracle cannot take the whole batch in seconds, so the
 check is on sampled sequences (the shortest, the longest and one seeded other; two of the four
 where all four hold 131072 tokens; the first, the last and one seeded other where all hold 32768): all their outputs against the oracle (f32 output to max abs /
 rel L2 2e-3, bf16 output within one bf16 ulp or 2e-3), and their pool rows -- codes, scales and
@@ -63,9 +64,10 @@ def full():
         pool.close()
 
 
-def _step(w, pool, kn, vn, out_f32, engine=kvq.ENGINE_AUTO):
+def _step(w, pool, kn, vn, out_f32, engine=kvq.ENGINE_AUTO, partition_tokens=kvq.PARTITION_AUTO):
     out = kvq.decode_step(G.u16_dev(w.q_bits), G.u16_dev(kn), G.u16_dev(vn), pool, G.i32_dev(w.table),
-                          G.i32_dev(w.lengths), w.scale, w.max_len, out_f32=out_f32, engine=engine)
+                          G.i32_dev(w.lengths), w.scale, w.max_len, out_f32=out_f32, engine=engine,
+                          partition_tokens=partition_tokens)
     torch.cuda.synchronize()
     if out_f32:
         return out.cpu().numpy().astype(np.float64)
@@ -86,6 +88,11 @@ def test_full_size_step_on_sampled_sequences(full, name):
     if w.bits == 4 and w.D == 256:
         got_m = _step(w, pool, kn, vn, out_f32=True, engine=kvq.ENGINE_MATRIX)
         G.check_f32(got_m[seqs], ref, tag=f"{name} matrix engine seqs {seqs}")
+    if name.startswith("c4"):
+        # the c4 shapes' stated partition counts: 1, 16 and 256 partitions of a 131072-token sequence
+        for pt in (131072, 8192, 512):
+            got_p = _step(w, pool, kn, vn, out_f32=True, partition_tokens=pt)
+            G.check_f32(got_p[seqs], ref, tag=f"{name} partitions of {pt} seqs {seqs}")
 
     print("  outputs match; pool rows", flush=True)
     # integer parts: the sampled sequences' rows (the N the step appended included) against the
