@@ -273,7 +273,10 @@ class Bench:
                "partial_pass_us": round(float(np.mean(t["par"])) * 1e3, 2),
                "merge_us_events": round(float(np.mean(t["mer"])) * 1e3, 2),
                "kernels_us": {k: round(v * 1e3, 2) for k, v in t["kern"].items()},
-               "partition_tokens": pt, "settle_steps": settle, "_t": t}
+               "partition_tokens": pt,
+               "engine_used": "matrix" if self.kvq.paged_decode_engine(self.pool, shp) == self.kvq.ENGINE_MATRIX
+                              else "vector",
+               "settle_steps": settle, "_t": t}
         log(f"[bench] {label or w.name}: {t['ms'] * 1e3:.1f} us/step (events: median "
             f"{rec['step_us_events']['median']}, p10 {rec['step_us_events']['p10']}, p90 "
             f"{rec['step_us_events']['p90']}); kernels (library events): prep {t['kern']['prep'] * 1e3:.1f}, "
@@ -438,8 +441,8 @@ def main():
                          flush=flush, label=f"{w.name} ({args.engine} engine)")
     t = head.pop("_t")
     eff = w.effective_bytes()
-    src_hash = kernel_source_hash() if args.engine != "matrix" else None
-    roof = roofline(w, t["kern"]["partial"], args.engine, src_hash)
+    src_hash = kernel_source_hash() if head["engine_used"] == "vector" else None
+    roof = roofline(w, t["kern"]["partial"], head["engine_used"], src_hash)
 
     def matrix_ok(wl):
         return wl.bits == 4 and wl.group == 64 and wl.D in (128, 256) and wl.DV == wl.D
@@ -460,7 +463,8 @@ def main():
         bd = Bench(kvq, torch, wd, dev)
         rd = bd.measure(kvq.ENGINE_AUTO, args.steps, args.warmup, flush=flush, label="diag (vector engine)")
         kd = rd.pop("_t")["kern"]["partial"]
-        rd["roofline"] = roofline(wd, kd, "auto", src_hash)
+        rd["roofline"] = roofline(wd, kd, rd["engine_used"],
+                                  kernel_source_hash() if rd["engine_used"] == "vector" else None)
         rd["config"] = {"workload": f"diag: 4-bit affine g64 paged KV, B={wd.B} x {wd.max_len} tokens, BS={wd.BS}, "
                                     f"HQ={wd.HQ}, HK={wd.HK}, D={wd.D}, N={wd.N}"}
         rd["effective_bytes"] = wd.effective_bytes()
@@ -482,7 +486,8 @@ def main():
                                 f"N={w.N}") if (w.name == "c3" and not over) else
                                (w.name + "".join(f" {k}={v}" for k, v in over.items())),
                    "global_batch": w.B, "seq_len": w.max_len, "parallelism": "single GPU",
-                   "partition_tokens": head["partition_tokens"], "engine": args.engine},
+                   "partition_tokens": head["partition_tokens"], "engine": args.engine,
+                   "engine_used": head["engine_used"]},
         "us_per_step": head["us_per_step"], "pct_hbm_peak": head["pct_hbm_peak"],
         "step_us_events": head["step_us_events"], "effective_bytes": eff,
         "kernels_us": head["kernels_us"], "partial_pass_us": head["partial_pass_us"],

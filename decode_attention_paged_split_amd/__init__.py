@@ -26,7 +26,7 @@ from typing import Dict, Optional, Sequence
 __all__ = [
     "KvqError", "PoolDesc", "DecodeShape", "Pool", "decode", "lib", "kv_pool_create", "kv_pool_wrap",
     "kv_pool_destroy", "kv_pool_plane_bytes", "kv_append_quantize", "paged_decode_workspace_bytes",
-    "paged_decode_partition_tokens", "paged_decode_attention", "paged_decode_partial",
+    "paged_decode_partition_tokens", "paged_decode_engine", "paged_decode_attention", "paged_decode_partial",
     "paged_decode_merge", "paged_decode_step", "paged_decode_step_partial", "paged_decode_step_noalloc",
     "NOALLOC_WORKSPACE_BYTES", "kv_gather_debug", "make_shape", "gather", "decode_step",
     "kvq_timing_enable", "kvq_timing_read", "kvq_probe_read", "kvq_probe_read_ex", "kvq_probe_pool_read", "TIMING_PREP", "TIMING_PARTIAL", "TIMING_MERGE", "PARTITION_AUTO", "PARTITION_STREAM",
@@ -93,6 +93,7 @@ def lib() -> ctypes.CDLL:
             "kv_append_quantize": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P]),
             "paged_decode_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.POINTER(DecodeShape)]),
             "paged_decode_partition_tokens": (ctypes.c_int32, [_P, ctypes.POINTER(DecodeShape)]),
+            "paged_decode_engine": (ctypes.c_int32, [_P, ctypes.POINTER(DecodeShape)]),
             "paged_decode_attention": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_float,
                                                       ctypes.POINTER(DecodeShape), _P, ctypes.c_size_t,
                                                       _P, _P]),
@@ -222,6 +223,14 @@ def paged_decode_workspace_bytes(pool: "Pool", shape: DecodeShape) -> int:
 
 def paged_decode_partition_tokens(pool: "Pool", shape: DecodeShape) -> int:
     return int(lib().paged_decode_partition_tokens(pool.handle, ctypes.byref(shape)))
+
+
+def paged_decode_engine(pool: "Pool", shape: DecodeShape) -> int:
+    """ENGINE_VECTOR or ENGINE_MATRIX: the engine this shape runs on (the automatic choice resolved)."""
+    r = int(lib().paged_decode_engine(pool.handle, ctypes.byref(shape)))
+    if r < 0:
+        _check(r)
+    return r
 
 
 def paged_decode_attention(q, pool: "Pool", block_table, lengths, scale: float, shape: DecodeShape,

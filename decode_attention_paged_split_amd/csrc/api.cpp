@@ -107,20 +107,33 @@ int qvw_for(int qv, int bits, int D, int DV, int gs) {
   return 1;
 }
 
-// Tokens per split-K partition for the fixed-partition schedule; 0 selects the balanced
-// stream schedule (every wave gets an equal share of all cached tokens).  KVQ_PARTITION_TOKENS
-// (> 0) overrides an automatic choice, for sweeps.
-bool use_mfma(const kvq_decode_shape* s) { return s->engine == KVQ_ENGINE_MATRIX; }
+// The engine of the partial pass: the matrix cores when asked for, or (automatic choice) when a
+// KV head carries at least one full MFMA column block of query vectors (REP * N >= 16: several
+// query rows per sequence, a matrix-matrix product per KV head, which the pages' multi-row
+// kernel also gives to the matrix unit), the format is one the matrix engine reads and the
+// schedule is the stream; else the vector ALU (single-row decode: a matrix-vector product).
+bool use_mfma(const kvq_pool* pool, const kvq_decode_shape* s) {
+  if (s->engine == KVQ_ENGINE_MATRIX) return true;
+  if (s->engine != KVQ_ENGINE_AUTO || s->partition_tokens > 0) return false;
+  const kvq_pool_desc& d = pool->desc;
+  if (d.num_kv_heads < 1 || s->num_q_heads % d.num_kv_heads != 0) return false;
+  const int qv = (s->num_q_heads / d.num_kv_heads) * s->q_rows;
+  return qv >= kvq::MFMA_QVW && kvq::mfma_supported(d.bits, d.head_dim, d.group_size) &&
+         d.v_head_dim == d.head_dim;
+}
 int qgroups_of(const kvq_pool* pool, const kvq_decode_shape* s);
 
+// Tokens per split-K partition for the fixed-partition schedule; 0 selects the balanced
+// stream schedule (every wave gets an equal share of all cached tokens).  KVQ_PARTITION_TOKENS
+// (> 0) overrides an automatic choice of the vector engine, for sweeps.
 int choose_partition(const kvq_pool* pool, const kvq_decode_shape* s) {
   if (s->partition_tokens > 0) return s->partition_tokens;
   if (s->partition_tokens == KVQ_PARTITION_STREAM) return 0;
+  if (use_mfma(pool, s)) return 0;
   if (const char* e = std::getenv("KVQ_PARTITION_TOKENS")) {
     const int v = std::atoi(e);
     if (v > 0) return v;
   }
-  if (use_mfma(s)) return 0;
   // A stream too short to give every compute unit a full range of 8 tiles (at most
   // B * max_len * HK * query groups tokens: the lengths themselves are on the device) runs as
   // fixed partitions instead, sized so that there are about as many partitions as compute
@@ -145,7 +158,7 @@ struct StreamGeom {
 };
 
 StreamGeom stream_geom(const kvq_pool* pool, const kvq_decode_shape* s) {
-  if (use_mfma(s)) {
+  if (use_mfma(pool, s)) {
     const bool split = pool->desc.head_dim == 256;
     int per_cu = split ? 4 : 8;
     if (const char* e = std::getenv("KVQ_MFMA_RANGES_PER_CU")) per_cu = std::max(2, std::min(16, std::atoi(e)));
@@ -172,7 +185,7 @@ int stream_lanes(int qgroups, int pt, bool mfma) {
 // query vectors per workgroup (vector ALU) or per wave (matrix cores, padded to 16)
 int qvw_of(const kvq_pool* pool, const kvq_decode_shape* s) {
   const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
-  if (use_mfma(s))
+  if (use_mfma(pool, s))
     return (pool->desc.head_dim == 256 && qv <= kvq::MFMA_PAIR_QVW) ? kvq::MFMA_PAIR_QVW : kvq::MFMA_QVW;
   return qvw_for(qv, pool->desc.bits, pool->desc.head_dim, pool->desc.v_head_dim, pool->desc.group_size);
 }
@@ -211,7 +224,7 @@ int validate_shape(const kvq_pool* pool, const kvq_decode_shape* s) {
   if (s->engine < KVQ_ENGINE_AUTO || s->engine > KVQ_ENGINE_MATRIX)
     return fail(KVQ_ERR_INVALID, "engine must be 0 (automatic), 1 (vector ALU) or 2 (matrix cores)");
   const kvq_pool_desc& pd = pool->desc;
-  if (use_mfma(s)) {
+  if (use_mfma(pool, s)) {
     if (!kvq::mfma_supported(pd.bits, pd.head_dim, pd.group_size) || pd.v_head_dim != pd.head_dim)
       return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core engine reads 4-bit pages with head_dim 128 or 256 "
                                        "(v_head_dim the same) and group_size 64");
@@ -247,7 +260,7 @@ WsLayout workspace_layout(const kvq_pool* pool, const kvq_decode_shape* s, int p
   WsLayout L{};
   L.ml_off = up(rows * pool->desc.v_head_dim * sizeof(float));
   L.qp_off = L.total = L.ml_off + rows * 2 * sizeof(float);
-  if (!use_mfma(s)) {
+  if (!use_mfma(pool, s)) {
     // the q copy, then kvq::Q_COPY_TAIL bytes the partial kernel's scalar-cache warm-up may read
     // past the last unit's copy (it requests whole groups of 64-byte lines)
     const size_t qv = (size_t)s->batch * pool->desc.num_kv_heads * qgroups_of(pool, s) * qvw_of(pool, s);
@@ -518,6 +531,11 @@ int32_t paged_decode_partition_tokens(const kvq_pool* pool, const kvq_decode_sha
   return choose_partition(pool, shape);
 }
 
+int32_t paged_decode_engine(const kvq_pool* pool, const kvq_decode_shape* shape) {
+  if (int r = validate_shape(pool, shape)) return r;
+  return use_mfma(pool, shape) ? KVQ_ENGINE_MATRIX : KVQ_ENGINE_VECTOR;
+}
+
 namespace {
 
 struct Plan {
@@ -571,7 +589,7 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   const kvq_pool_desc& d = pool->desc;
   const int parts = pt > 0 ? (shape->max_len + pt - 1) / pt : 0;
   P->qvw = qvw_of(pool, shape);
-  P->mfma = use_mfma(shape);
+  P->mfma = use_mfma(pool, shape);
 
   kvq::PartialArgs& a = P->a;
   a = kvq::PartialArgs{};

@@ -166,7 +166,11 @@ typedef struct kvq_decode_shape {
  *     128 or 256 (v_head_dim the same), the balanced stream only (partition_tokens <= 0).  It serves the GQA groups where the vector ALU
  *     rather than HBM bounds the pass ([P50] multi-query.ts puts a KV head's query rows on the
  *     matrix unit for the same reason).
- *   KVQ_ENGINE_AUTO: the vector engine. */
+ *   KVQ_ENGINE_AUTO: the matrix engine where it applies and a KV head carries at least 16 query
+ *     vectors (HQ / HK * q_rows >= 16: several query rows per sequence make the per-head work a
+ *     matrix-matrix product, which [P50] multi-query.ts also gives to the matrix unit) and
+ *     partition_tokens <= 0; else the vector engine (single-row decode, a matrix-vector product
+ *     bound by memory or the vector ALU).  paged_decode_engine reports the choice. */
 enum kvq_engine { KVQ_ENGINE_AUTO = 0, KVQ_ENGINE_VECTOR = 1, KVQ_ENGINE_MATRIX = 2 };
 
 /* Bytes of workspace paged_decode_attention needs for this shape (0 if the shape is invalid;
@@ -181,6 +185,10 @@ size_t paged_decode_workspace_bytes(const kvq_pool* pool, const kvq_decode_shape
 /* Partition size the library uses for this shape: the fixed partition's tokens, or 0 for the
  * balanced stream (for reporting). */
 int32_t paged_decode_partition_tokens(const kvq_pool* pool, const kvq_decode_shape* shape);
+
+/* Engine the library uses for this shape: KVQ_ENGINE_VECTOR or KVQ_ENGINE_MATRIX (the automatic
+ * choice resolved; for reporting), or a negative kvq_status if the shape is invalid for the pool. */
+int32_t paged_decode_engine(const kvq_pool* pool, const kvq_decode_shape* shape);
 
 /* Decode attention for N <= KVQ_MAX_Q_ROWS query rows per sequence read straight from the pages
  * ([P50] paged.ts pagedAttentionView.attend, direct route; kvq4-decode.ts):

@@ -333,3 +333,27 @@ def test_noalloc_step_refuses_shapes_beyond_its_scratch(lib):
     assert 0 < lib.paged_decode_workspace_bytes(p.handle, ctypes.byref(ok)) <= kvq.NOALLOC_WORKSPACE_BYTES
     assert lib.paged_decode_step_noalloc(P, None, P, p.handle, P, P, 1.0, ctypes.byref(ok), P, None) == -1
     p.close()
+
+
+@pytest.mark.parametrize("bits,D,HQ,HK,N,pt,engine,expect", [
+    (4, 256, 16, 2, 1, 0, 0, 1),      # single-row GQA 8: a matrix-vector product per KV head -> vector ALU
+    (4, 256, 8, 2, 1, 0, 0, 1),       # GQA 4, one row
+    (4, 256, 16, 2, 2, 0, 0, 2),      # 16 query vectors per KV head -> matrix cores
+    (4, 256, 32, 4, 4, 0, 0, 2),      # 4 rows x GQA 8 (32 vectors)
+    (4, 256, 32, 4, 4, -1, 0, 2),     # the stream asked for explicitly
+    (4, 256, 32, 4, 4, 64, 0, 1),     # fixed partitions: the vector engine
+    (4, 256, 32, 4, 4, 0, 1, 1),      # vector asked for
+    (4, 256, 16, 2, 1, 0, 2, 2),      # matrix asked for
+    (4, 128, 32, 4, 4, 0, 0, 2),      # head dim 128
+    (8, 128, 32, 4, 4, 0, 0, 1),      # 8-bit pages: the matrix engine does not read them
+    (16, 128, 32, 4, 4, 0, 0, 1),     # bf16 pages
+])
+def test_engine_choice(lib, bits, D, HQ, HK, N, pt, engine, expect):
+    """paged_decode_engine resolves the automatic choice: the matrix cores for 16+ query vectors
+    per KV head on 4-bit group-64 pages with the stream schedule, the vector ALU otherwise."""
+    p = _FakePool(bits=bits, HK=HK, D=D)
+    s = kvq.DecodeShape(2, HQ, N, 40, 1000, pt, 0, engine)
+    assert lib.paged_decode_engine(p.handle, ctypes.byref(s)) == expect, lib.kvq_last_error()
+    s.engine = 3
+    assert lib.paged_decode_engine(p.handle, ctypes.byref(s)) == -1
+    p.close()

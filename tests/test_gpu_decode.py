@@ -103,9 +103,12 @@ def test_decode_edge_cases(filled, case):
     name = case.pop("name")
     print(f"edge {name} {case}", flush=True)
     w, pool, ref = filled(name, **case)
-    for pt in (kvq.PARTITION_STREAM, kvq.PARTITION_AUTO, 7):
-        got = G.run_decode(w, pool, partition_tokens=pt)
-        G.check_f32(got, ref, tag=f"{name} {case} pt={pt}")
+    # the automatic engine (the matrix cores for 16+ query vectors per KV head on 4-bit pages), and
+    # the vector engine's stream explicitly
+    for pt, engine in ((kvq.PARTITION_STREAM, kvq.ENGINE_AUTO), (kvq.PARTITION_AUTO, kvq.ENGINE_AUTO),
+                       (7, kvq.ENGINE_AUTO), (kvq.PARTITION_STREAM, kvq.ENGINE_VECTOR)):
+        got = G.run_decode(w, pool, partition_tokens=pt, engine=engine)
+        G.check_f32(got, ref, tag=f"{name} {case} pt={pt} engine={engine}")
 
 
 @pytest.mark.parametrize("name", ["c2", "c3", "c4_8"])

@@ -4,7 +4,7 @@ Each workload is built at its full size (every sequence, every cached token), th
 the append kernel with every row but each sequence's last N, and one decode step run as the bench
 runs it (paged_decode_step: the step's new rows appended at the slots the block table gives them,
 the partial pass with the automatic schedule and engine, the merge; for the 4-bit head-dim-256
-workloads also the matrix-core variant, for the c4 shapes also 1, 16 and 256 fixed partitions per
+workloads also each engine explicitly, for the c4 shapes also 1, 16 and 256 fixed partitions per
 131072-token sequence).  The oracle cannot take the whole batch in seconds, so the
 check is on sampled sequences (the shortest, the longest and one seeded other; two of the four
 where all four hold 131072 tokens; the first, the last and one seeded other where all hold 32768): all their outputs against the oracle (f32 output to max abs /
@@ -86,8 +86,11 @@ def test_full_size_step_on_sampled_sequences(full, name):
     G.check_f32(got[seqs], ref, tag=f"{name} seqs {seqs}")
     G.check_bf16(bits[seqs], ref, tag=f"{name} seqs {seqs}")
     if w.bits == 4 and w.D == 256:
-        got_m = _step(w, pool, kn, vn, out_f32=True, engine=kvq.ENGINE_MATRIX)
-        G.check_f32(got_m[seqs], ref, tag=f"{name} matrix engine seqs {seqs}")
+        # both engines explicitly (the automatic choice is the matrix cores for c5's 32 query
+        # vectors per KV head, the vector ALU for the single-row shapes)
+        for engine, label in ((kvq.ENGINE_MATRIX, "matrix"), (kvq.ENGINE_VECTOR, "vector")):
+            got_e = _step(w, pool, kn, vn, out_f32=True, engine=engine)
+            G.check_f32(got_e[seqs], ref, tag=f"{name} {label} engine seqs {seqs}")
     if name.startswith("c4"):
         # the c4 shapes' stated partition counts: 1, 16 and 256 partitions of a 131072-token sequence
         for pt in (131072, 8192, 512):
