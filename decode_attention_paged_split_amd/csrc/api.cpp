@@ -168,12 +168,16 @@ StreamGeom stream_geom(const kvq_pool* pool, const kvq_decode_shape* s) {
   return {device_cus(), kvq::VALU_STREAM_WAVES, kvq::VALU_STREAM_WAVES * kvq::VALU_TILE};
 }
 
-// Vector-engine stream: the query groups of one KV head worked side by side on one range, by L
+// Stream schedule: the query groups of one KV head worked side by side on one range, by L
 // workgroups on one XCD (one group each), so that each K/V row is fetched from memory once for
-// all of them: 4 when the groups come in fours, 2 when in pairs, else 1.  KVQ_STREAM_LANES (1, 2 or 4,
+// all of them: 4 when the groups come in fours, 2 when in pairs, else 1 (the vector engine, and
+// the matrix engine's head-dim-256 kernel for 16-vector groups).  KVQ_STREAM_LANES (1, 2 or 4,
 // dividing the group count) overrides, for measurements.
-int stream_lanes(int qgroups, int pt, bool mfma) {
-  if (pt != 0 || mfma) return 1;
+int stream_lanes(int qgroups, int pt, bool mfma, int qvw, int head_dim) {
+  if (pt != 0) return 1;
+  // the matrix engine runs side-by-side groups in its head-dim-256 kernel for more than 8 vectors
+  // per KV head (the split kernel, one 16-vector group per workgroup)
+  if (mfma && !(head_dim == 256 && qvw == kvq::MFMA_QVW)) return 1;
   int L = qgroups % 4 == 0 ? 4 : (qgroups % 2 == 0 ? 2 : 1);
   if (const char* e = std::getenv("KVQ_STREAM_LANES")) {
     const int v = std::atoi(e);
@@ -613,7 +617,7 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   a.len_cap = (int)std::min<long>(shape->max_len, (long)shape->max_blocks_per_seq * d.block_size);
   const StreamGeom sg = stream_geom(pool, shape);
   a.batch = shape->batch; a.num_ranges = sg.ranges; a.range_sub = sg.sub; a.min_tokens = sg.min_tokens;
-  a.lanes = stream_lanes(a.qgroups, pt, P->mfma);
+  a.lanes = stream_lanes(a.qgroups, pt, P->mfma, P->qvw, d.head_dim);
   if (a.lanes > 1) a.num_ranges = std::max(1, a.num_ranges / a.lanes);   // L workgroups per range
 
   P->merge_threads = merge_threads_for(d.v_head_dim, pt, parts, sg,

@@ -21,7 +21,7 @@ partial_mfma_kernel(PartialArgs a) {
   const int qv = lane & 15, ks = lane >> 4;       // query vector (MFMA n / m%16), k-slot (lane / 16)
 
   MfRange rg;
-  if (!mf_find_range(a, w, lane, rg)) return;      // no block-level barriers in this kernel
+  if (!mf_find_range(a, w, lane, rg, HQG)) return;      // no block-level barriers in this kernel
   int b = rg.b, len = rg.len, uu = rg.uu, t_lo = rg.t_lo;
   const int64_t x0 = rg.x0, x1 = rg.x1;
 

@@ -246,9 +246,10 @@ struct MfRange {
 };
 
 // Range `w` of the stream split into at most num_ranges equal ranges of at least min_tokens
-// tokens; false if range w is empty.
-__device__ __forceinline__ bool mf_find_range(const PartialArgs& a, int w, int lane, MfRange& r) {
-  const int B = a.batch, HQG = a.HK * a.qgroups;
+// tokens; false if range w is empty.  HQG: stream units per sequence (KV heads x query groups, or
+// x sets of `lanes` groups where those run side by side); r.uu is the unit (or set) index.
+__device__ __forceinline__ bool mf_find_range(const PartialArgs& a, int w, int lane, MfRange& r, int HQG) {
+  const int B = a.batch;
   int64_t tot = 0;
   for (int c = 0; c < B; c += 64) {
     const int bb = c + lane;
@@ -291,6 +292,20 @@ __device__ __forceinline__ bool mf_find_range(const PartialArgs& a, int w, int l
   r.uu = mf_uni((int)(rem / r.len));
   r.t_lo = mf_uni((int)(rem - (int64_t)r.uu * r.len));
   return true;
+}
+
+// Range and lane of workgroup i of nwg when the L query groups of a set run side by side, one
+// workgroup each: workgroups are handed to the 8 XCDs in turn by index, so the L workgroups of a
+// range are taken 8 apart (one XCD, one L2) and an XCD's ranges are consecutive.
+__device__ __forceinline__ void mf_range_lane(int L, int i, int nwg, int& w, int& ln) {
+  if (L > 1 && nwg % (8 * L) == 0) {
+    const int q = i >> 3;
+    ln = q % L;
+    w = (i & 7) * (nwg / (8 * L)) + q / L;
+  } else {
+    ln = i % L;
+    w = i / L;
+  }
 }
 
 // max / sum over the four lanes that share a query vector (lane, lane ^ 16, ^ 32, ^ 48)

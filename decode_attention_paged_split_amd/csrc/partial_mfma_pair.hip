@@ -52,7 +52,7 @@ partial_mfma_pair_kernel(PartialArgs a) {
   const uint32_t sel1 = bx ? 0x03020C0Cu : 0x0C0C0302u;
 
   MfRange rg;
-  if (!mf_find_range(a, w, lane, rg)) return;     // the same for both waves: no barrier is left
+  if (!mf_find_range(a, w, lane, rg, HQG)) return;     // the same for both waves: no barrier is left
   int b = rg.b, len = rg.len, uu = rg.uu, t_lo = rg.t_lo;
   const int64_t x1 = rg.x1;
   const int REP = a.HQ / a.HK, N = a.N;

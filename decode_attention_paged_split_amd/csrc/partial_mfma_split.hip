@@ -12,13 +12,19 @@ partial_mfma_split_kernel(PartialArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int h = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // dim half of this wave
-  const int w = blockIdx.x;                                         // range (whole workgroup)
+  // this workgroup's range and lane: the L = a.lanes query groups of a set (KV head, L
+  // consecutive groups) run side by side on L workgroups of one XCD, one group each, over the same
+  // range, so each K/V row is fetched from memory once for the set
+  int w, ln;
+  mf_range_lane(a.lanes, blockIdx.x, gridDim.x, w, ln);
+  w = __builtin_amdgcn_readfirstlane(w);
+  ln = __builtin_amdgcn_readfirstlane(ln);
   SpWave& S = sh.w[h];
-  const int B = a.batch, HQG = a.HK * a.qgroups;
+  const int B = a.batch, L = a.lanes, QGB = a.qgroups / L, HS = a.HK * QGB;   // sets per sequence
   const int qv = lane & 15, ks = lane >> 4;
 
   MfRange rg;
-  if (!mf_find_range(a, w, lane, rg)) return;     // the same for both waves: no barrier is left
+  if (!mf_find_range(a, w, lane, rg, HS)) return;  // the same for both waves: no barrier is left
   int b = rg.b, len = rg.len, uu = rg.uu, t_lo = rg.t_lo;
   const int64_t x1 = rg.x1;
   const int REP = a.HQ / a.HK, N = a.N;
@@ -29,7 +35,7 @@ partial_mfma_split_kernel(PartialArgs a) {
   while (x < x1) {
     const int seg = (int)min<int64_t>((int64_t)(len - t_lo), x1 - x);
     const int t1 = t_lo + seg;
-    const int hk = uu / a.qgroups, qg = uu - hk * a.qgroups;
+    const int hk = uu / QGB, qg = (uu - hk * QGB) * L + ln;
     const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
 
     // ---- q^T fragments of this lane's query vector over the wave's dims (zero for padding)
@@ -231,7 +237,7 @@ partial_mfma_split_kernel(PartialArgs a) {
     l = qv_sum(l);
 #pragma unroll
     for (int g = 0; g < SP_G; ++g) pbias[g] = qv_sum(pbias[g]);
-    const int64_t slot = (int64_t)b * HQG + uu + w;
+    const int64_t slot = ((int64_t)b * HS + uu + w) * L + ln;
     if (qreal) {
       float* orow = a.opart + (slot * MF_QV + qv) * D + SP_HD * h;
       constexpr float two24 = 16777216.0f;        // the V codes entered as c * 2^-24
@@ -253,7 +259,7 @@ partial_mfma_split_kernel(PartialArgs a) {
     t_lo += seg;
     if (t_lo >= len && x < x1) {
       t_lo = 0;
-      if (++uu == HQG) {
+      if (++uu == HS) {
         uu = 0;
         do { ++b; } while (b < B && mf_len(a, b) == 0);
         if (b >= B) break;
@@ -264,7 +270,7 @@ partial_mfma_split_kernel(PartialArgs a) {
 }
 
 hipError_t launch_mfma_split(const PartialArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(partial_mfma_split_kernel, dim3((unsigned)a.num_ranges), dim3(2 * 64), 0, s, a);
+  hipLaunchKernelGGL(partial_mfma_split_kernel, dim3((unsigned)(a.num_ranges * a.lanes)), dim3(2 * 64), 0, s, a);
   return hipGetLastError();
 }
 

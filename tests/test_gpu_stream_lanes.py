@@ -7,7 +7,9 @@ lanes' partial slots interleave per range and the merge reads them back by lane.
 Checked against the oracle (f32 output, max abs and rel L2 2e-3):
 - the c5 shape (4-bit, 32 query vectors per KV head: 4 groups) with the lane count forced to
   1, 2 and 4 (KVQ_STREAM_LANES), ragged lengths, one sequence given length 0 (its output zero, the others unchanged);
-- group counts 2, 3 and 6 (automatic lanes 2, 1, 2) on a bf16 and a 4-bit pool.
+- group counts 2, 3 and 6 (automatic lanes 2, 1, 2) on a bf16 and a 4-bit pool;
+- the matrix engine's head-dim-256 kernel (groups of 16 vectors) at 2 and 4 groups per KV head,
+  lanes forced to 1, 2 and 4.
 Every output comes from libkvq through the C ABI."""
 import os
 
@@ -22,14 +24,14 @@ from workloads import make_workload
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, lanes=None, lengths=None):
+def _run(w, lanes=None, lengths=None, engine=kvq.ENGINE_VECTOR):
     pool = G.new_pool(w)
     G.fill_pool(w, pool)
     old = os.environ.get("KVQ_STREAM_LANES")
     try:
         if lanes is not None:
             os.environ["KVQ_STREAM_LANES"] = str(lanes)
-        return G.run_decode(w, pool, partition_tokens=kvq.PARTITION_STREAM, engine=kvq.ENGINE_VECTOR,
+        return G.run_decode(w, pool, partition_tokens=kvq.PARTITION_STREAM, engine=engine,
                             lengths=None if lengths is None else G.i32_dev(lengths))
     finally:
         if old is None:
@@ -61,4 +63,19 @@ def test_group_counts(name, N):
     ref = attention.workload_output(w)
     got = _run(w)
     err, rl2 = G.check_f32(got, ref, tag=f"{name} N={N}")
+    print(f"  max abs {err:.2e} rel L2 {rl2:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("N,lanes", [(4, 1), (4, 2), (8, 2), (8, 4)])
+def test_matrix_engine_groups_side_by_side(N, lanes):
+    # the matrix engine's head-dim-256 kernel takes 16 vectors per group: 4 rows x GQA 8 = 2 groups,
+    # 8 rows = 4 groups
+    print(f"matrix engine c5 N={N} lanes {lanes}", flush=True)
+    w = make_workload("c5", B=3, len_lo=300, len_hi=2000, N=N, HQ=16, HK=2)
+    ref = attention.workload_output(w)
+    lengths = w.lengths.astype(np.int32).copy()
+    lengths[1] = 0
+    got = _run(w, lanes, lengths, engine=kvq.ENGINE_MATRIX)
+    err, rl2 = G.check_f32(got[[0, 2]], ref[[0, 2]], tag=f"matrix N={N} lanes {lanes}")
+    assert np.all(got[1] == 0.0)
     print(f"  max abs {err:.2e} rel L2 {rl2:.2e}", flush=True)
