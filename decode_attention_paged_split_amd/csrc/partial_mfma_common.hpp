@@ -294,20 +294,6 @@ __device__ __forceinline__ bool mf_find_range(const PartialArgs& a, int w, int l
   return true;
 }
 
-// Range and lane of workgroup i of nwg when the L query groups of a set run side by side, one
-// workgroup each: workgroups are handed to the 8 XCDs in turn by index, so the L workgroups of a
-// range are taken 8 apart (one XCD, one L2) and an XCD's ranges are consecutive.
-__device__ __forceinline__ void mf_range_lane(int L, int i, int nwg, int& w, int& ln) {
-  if (L > 1 && nwg % (8 * L) == 0) {
-    const int q = i >> 3;
-    ln = q % L;
-    w = (i & 7) * (nwg / (8 * L)) + q / L;
-  } else {
-    ln = i % L;
-    w = i / L;
-  }
-}
-
 // max / sum over the four lanes that share a query vector (lane, lane ^ 16, ^ 32, ^ 48)
 __device__ __forceinline__ float qv_max(float x) { return block_reduce<OpMax, 16, 64>(x); }
 __device__ __forceinline__ float qv_sum(float x) { return block_reduce<OpAdd, 16, 64>(x); }

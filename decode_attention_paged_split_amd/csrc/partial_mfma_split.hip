@@ -16,7 +16,7 @@ partial_mfma_split_kernel(PartialArgs a) {
   // consecutive groups) run side by side on L workgroups of one XCD, one group each, over the same
   // range, so each K/V row is fetched from memory once for the set
   int w, ln;
-  mf_range_lane(a.lanes, blockIdx.x, gridDim.x, w, ln);
+  stream_range_lane(a.lanes, blockIdx.x, gridDim.x, w, ln);
   w = __builtin_amdgcn_readfirstlane(w);
   ln = __builtin_amdgcn_readfirstlane(ln);
   SpWave& S = sh.w[h];

@@ -904,24 +904,14 @@ partial_stream_kernel(PartialArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int B = a.batch;
   // Lanes: the L query groups of a set (KV head, L consecutive groups) run side by side on L
-  // workgroups, one group each, over the same range of the set stream, so each K/V row comes from
-  // memory once for the set and the other lanes find it in the L2 cache.  Workgroups are handed
-  // to the 8 XCDs (each with its own L2) in turn by index, so the L workgroups of a range are
-  // taken 8 apart: index i runs on XCD i mod 8, and the ranges of one XCD are consecutive.
+  // workgroups of one XCD, one group each, over the same range of the set stream, so each K/V row
+  // comes from memory once for the set and the other lanes find it in that XCD's L2 cache.
   // L = 1: one workgroup per range, every group in turn.
   const int L = a.lanes;
   int g, ln;                                                     // this workgroup's range, lane
-  {
-    const int i = blockIdx.x, nwg = gridDim.x;
-    if (L > 1 && nwg % (8 * L) == 0) {
-      const int q = i >> 3;
-      ln = q % L;
-      g = (i & 7) * (nwg / (8 * L)) + q / L;
-    } else {
-      ln = i % L;
-      g = i / L;
-    }
-  }
+  stream_range_lane(L, blockIdx.x, gridDim.x, g, ln);
+  g = uni(g);
+  ln = uni(ln);
   const int QGB = a.qgroups / L, HS = a.HK * QGB;                // sets per KV head, per sequence
 
   // total stream length T (set positions) and the number of working ranges (every wave computes
