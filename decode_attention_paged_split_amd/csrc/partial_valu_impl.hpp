@@ -377,13 +377,17 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
   constexpr int GV = Gv::G, NPV = Gv::NP, KCPV = Gv::KCP, ROWBV = Gv::ROWB, KPBV = Gv::KPB;
   constexpr bool AFF = Gm::AFF;
   constexpr int QBS = Q_BLOCK_WORDS;                              // words per q block
-  // Rows of one part (<= 128 bytes; K no wider than V) are loaded coalesced, a tile's 64 rows as
-  // 64 * KCP pieces in token order, and reach their token's lane through LDS: V's by the staging
-  // the V phase does anyway, K's by a round trip at the top of the tile.  Wider rows, rows of 48
-  // or 96 bytes (3- and 6-bit codes at head dim 128) and rows under 64 bytes (where the K round
-  // trip costs more than it saves: 2-bit codes at head dim 128 measured 1.4 % slower) are loaded
-  // one token per lane.
-  constexpr bool COAL = NP == 1 && NPV == 1 && KPB <= KPBV && KCP >= 4 && 64 % KCP == 0 && 64 % KCPV == 0;
+  // Row parts of 64 to 128 bytes (K's no wider than V's) are loaded coalesced, a part of a tile's
+  // 64 rows as 64 * KCP pieces in token order, and reach their token's lane through LDS: V's by
+  // the staging the V phase does anyway, K's by a round trip before the part is used.  Rows of one
+  // part, and affine rows of two parts at scale groups of 64 or more (8-bit at head dim 256: 7 %
+  // faster); wider rows and 8-bit head-dim-256 rows at group 32 would spill registers, and bf16
+  // rows of two parts measured 2.5 % slower (c2: a few tiles per wave, the K round trip adds
+  // latency that nothing hides).  Parts of 48, 80 or
+  // 96 bytes (3-, 5- and 6-bit codes) and parts under 64 bytes (where the K round trip costs more
+  // than it saves: 2-bit codes at head dim 128 measured 1.4 % slower) are loaded one token per lane.
+  constexpr bool COAL = ((NP == 1 && NPV == 1) || (NP == 2 && NPV == 2 && GS >= 64 && AFF)) &&
+                        KPB <= KPBV && KCP >= 4 && 64 % KCP == 0 && 64 % KCPV == 0;
   int tt = uni(grab());
   if (tt >= t1) return;
   int tn_raw = grab();
@@ -513,7 +517,10 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
 #pragma unroll
     for (int h = 0; h < NP; ++h) {
       RowPart<KCP> knext;
-      if (h + 1 < NP) knext = load_row_part<KCP>(kplane, row, ROWB, (h + 1) * KPB);
+      if (h + 1 < NP) {
+        if constexpr (COAL) knext = load_rows_coalesced<KCP>(kplane + (h + 1) * KPB, row, ROWB, lane);
+        else knext = load_row_part<KCP>(kplane, row, ROWB, (h + 1) * KPB);
+      }
 #pragma unroll
       for (int gp = 0; gp < GPP; ++gp) {
         const int g = h * GPP + gp;                               // scale group
@@ -558,7 +565,10 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
           }
         }
       }
-      if (h + 1 < NP) kpart = knext;
+      if (h + 1 < NP) {
+        if constexpr (COAL) kpart = own_k_row(knext);
+        else kpart = knext;
+      }
     }
 
     // ---- stage V part 0 of this tile, then start the next tile's loads.  After a wave's last
@@ -623,7 +633,10 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
 #pragma unroll
     for (int h = 0; h < NPV; ++h) {
       RowPart<KCPV> vnext;
-      if (h + 1 < NPV) vnext = load_row_part<KCPV>(vplane, row, ROWBV, (h + 1) * KPBV);
+      if (h + 1 < NPV) {
+        if constexpr (COAL) vnext = load_rows_coalesced<KCPV>(vplane + (h + 1) * KPBV, row, ROWBV, lane);
+        else vnext = load_row_part<KCPV>(vplane, row, ROWBV, (h + 1) * KPBV);
+      }
       if (h > 0) {
         stage_v(vpart);
         wave_lds_sync();
