@@ -186,6 +186,21 @@ int stream_lanes(int qgroups, int pt, bool mfma, int qvw, int head_dim) {
   return L;
 }
 
+// Vector engine, stream schedule: positions charged per set that has tokens, ahead of its tokens.
+// A wave that changes sets inside its range writes its partial of the old set and waits for the
+// new set's q copy and first rows (about 9 us per wave on the 4-bit GQA-8 workload with ragged
+// lengths, measured with per-wave timestamps); ranges holding a set change finished 6.5 us later
+// than the others, and the slowest of them set the kernel's end.  The charge gives such a range
+// that many fewer tokens (the kernel drops it where no range holds a set change: equal lengths
+// whose sets divide the ranges evenly).  512 measured best (partial kernel on that workload
+// 172 -> 162 us; 4-row 4-bit 2,157 -> 2,137 us; bf16 GQA-4 35.8 -> 34.9 us).  KVQ_SET_COST
+// (0 .. 4096 tokens) overrides, for measurements.
+int stream_set_cost() {
+  int c = kvq::VALU_SET_COST;
+  if (const char* e = std::getenv("KVQ_SET_COST")) c = std::max(0, std::min(4096, std::atoi(e)));
+  return c;
+}
+
 // query vectors per workgroup (vector ALU) or per wave (matrix cores, padded to 16)
 int qvw_of(const kvq_pool* pool, const kvq_decode_shape* s) {
   const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
@@ -222,8 +237,9 @@ int validate_shape(const kvq_pool* pool, const kvq_decode_shape* s) {
   if (pt > 0 && (s->max_len + pt - 1) / pt > MAX_PARTS)
     return fail(KVQ_ERR_UNSUPPORTED, "more than %d partitions (max_len %d, partition %d)", MAX_PARTS,
                 s->max_len, pt);
-  if ((double)s->batch * s->max_len * pool->desc.num_kv_heads * qgroups_of(pool, s) >= 1099511627776.0)
-    return fail(KVQ_ERR_UNSUPPORTED, "batch * max_len * num_kv_heads * query groups must stay below 2^40");
+  // (stream positions: up to 4096 set-cost positions per set ride on top of the tokens)
+  if ((double)s->batch * (s->max_len + 4096.0) * pool->desc.num_kv_heads * qgroups_of(pool, s) >= 1099511627776.0)
+    return fail(KVQ_ERR_UNSUPPORTED, "batch * (max_len + 4096) * num_kv_heads * query groups must stay below 2^40");
   const int qv = (s->num_q_heads / pool->desc.num_kv_heads) * s->q_rows;
   if (s->engine < KVQ_ENGINE_AUTO || s->engine > KVQ_ENGINE_MATRIX)
     return fail(KVQ_ERR_INVALID, "engine must be 0 (automatic), 1 (vector ALU) or 2 (matrix cores)");
@@ -619,6 +635,7 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   a.batch = shape->batch; a.num_ranges = sg.ranges; a.range_sub = sg.sub; a.min_tokens = sg.min_tokens;
   a.lanes = stream_lanes(a.qgroups, pt, P->mfma, P->qvw, d.head_dim);
   if (a.lanes > 1) a.num_ranges = std::max(1, a.num_ranges / a.lanes);   // L workgroups per range
+  a.set_cost = (pt == 0 && !P->mfma) ? stream_set_cost() : 0;
 
   P->merge_threads = merge_threads_for(d.v_head_dim, pt, parts, sg,
                                        (double)shape->batch * d.num_kv_heads * a.qgroups,
@@ -633,6 +650,7 @@ int plan(const uint16_t* q, const kvq_pool* pool, const int32_t* block_table, co
   m.num_ranges = a.num_ranges; m.range_sub = a.range_sub; m.min_tokens = a.min_tokens;
   m.stream_combined = (pt == 0 && !P->mfma) ? 1 : 0;
   m.lanes = a.lanes;
+  m.set_cost = a.set_cost;
   return KVQ_OK;
 }
 

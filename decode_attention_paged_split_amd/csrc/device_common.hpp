@@ -107,6 +107,51 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // (one KV head's L consecutive groups) run side by side, one workgroup each, over the same range:
 // workgroups are handed to the 8 XCDs (each with its own L2) in turn by index, so the L workgroups
 // of a range are taken 8 indices apart (one XCD) and an XCD's ranges are consecutive.  L = 1: w = i.
+// Stream schedule: its length T in positions, the number R of working ranges and the set cost C in
+// force.  A set (a KV head's query groups worked together) of a sequence with tokens takes C
+// positions and then one per token.  C is the requested cost unless every range would hold the
+// same number of set changes anyway -- all sequences with tokens equally long, and the number of
+// sets S and the uncharged range count R0 dividing one another: then the set starts fall on
+// range boundaries (or every range holds S / R0 whole sets) and C is 0.  Every wave computes the
+// same, from the lengths clamped to [0, len_cap].
+struct StreamSpan {
+  int64_t T;
+  int R, C;
+};
+__device__ __forceinline__ StreamSpan stream_span(const int32_t* lengths, int B, int len_cap, int HS,
+                                                  int num_ranges, int min_tokens, int set_cost, int lane) {
+  long long tok = 0, nz = 0;
+  int lmin = 0x7fffffff, lmax = 0;
+  for (int c = 0; c < B; c += 64) {
+    const int bb = c + lane;
+    const int l = bb < B ? max(0, min(lengths[bb], len_cap)) : 0;
+    long long s = l, n = l > 0 ? 1 : 0;
+    int mn = l > 0 ? l : 0x7fffffff, mx = l;
+#pragma unroll
+    for (int off = 32; off >= 1; off /= 2) {
+      s += __shfl_xor(s, off, 64);
+      n += __shfl_xor(n, off, 64);
+      mn = min(mn, __shfl_xor(mn, off, 64));
+      mx = max(mx, __shfl_xor(mx, off, 64));
+    }
+    tok += s; nz += n; lmin = min(lmin, mn); lmax = max(lmax, mx);
+  }
+  tok = __builtin_amdgcn_readfirstlane((int)(tok & 0xffffffff)) |
+        ((long long)__builtin_amdgcn_readfirstlane((int)(tok >> 32)) << 32);
+  nz = __builtin_amdgcn_readfirstlane((int)nz);
+  lmin = __builtin_amdgcn_readfirstlane(lmin);
+  lmax = __builtin_amdgcn_readfirstlane(lmax);
+  const int64_t T0 = tok * HS, S = nz * HS;
+  const int R0 = (int)min<int64_t>((int64_t)num_ranges, (T0 + min_tokens - 1) / min_tokens);
+  int C = set_cost;
+  if (S > 0 && R0 > 0 && lmin == lmax && (R0 % S == 0 || S % R0 == 0)) C = 0;
+  StreamSpan r;
+  r.C = C;
+  r.T = T0 + S * C;
+  r.R = (int)min<int64_t>((int64_t)num_ranges, (r.T + min_tokens - 1) / min_tokens);
+  return r;
+}
+
 __device__ __forceinline__ void stream_range_lane(int L, int i, int nwg, int& w, int& ln) {
   if (L > 1 && nwg % (8 * L) == 0) {
     const int q = i >> 3;

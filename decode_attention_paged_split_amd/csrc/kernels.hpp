@@ -58,6 +58,7 @@ struct PartialArgs {
   int32_t min_tokens;       // stream: fewest tokens per working range
   int32_t len_cap;          // min(max_len, max_blocks * BS): lengths are clamped to [0, len_cap]
   int32_t lanes;            // vector stream: query groups of a KV head worked side by side (1, 2, 4)
+  int32_t set_cost;         // vector stream: positions charged per set that has tokens, ahead of them
 };
 
 struct MergeArgs {
@@ -70,6 +71,7 @@ struct MergeArgs {
   int32_t batch, HK, qgroups, qvw, num_ranges, range_sub, min_tokens;   // stream (part_tokens == 0)
   int32_t stream_combined;  // stream: a range's waves combined their partials of its last unit
   int32_t lanes;            // stream: query groups side by side per set (partial slots interleave)
+  int32_t set_cost;         // stream: positions charged per set that has tokens, ahead of them
 };
 
 // words per block of the vector engine's q copy: 16 bf16 pairs of one query vector, then (last
@@ -149,5 +151,8 @@ constexpr int MFMA_TILE = 64;
 // a range and shares its 64-token tiles among its waves
 constexpr int VALU_STREAM_WAVES = 8;
 constexpr int VALU_TILE = 64;
+// vector engine, stream schedule: positions charged per set ahead of its tokens (the cost of a
+// wave's change of set, in tokens; measured best at 512 on the workloads with ragged lengths)
+constexpr int VALU_SET_COST = 512;
 
 }  // namespace kvq

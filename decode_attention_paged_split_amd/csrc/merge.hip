@@ -13,10 +13,11 @@
 // LDS the same way.
 // Output is bf16 (round to nearest even) or f32.
 // Stream schedule: the stream of T set positions (a set: `lanes` consecutive query groups of one KV
-// head, worked side by side) is cut into R = min(num_ranges, ceil(T / min_tokens)) ranges; per
-// range it meets, a group owns range_sub consecutive slots from ((set + range) * lanes + lane) *
-// range_sub on -- or (stream_combined) the first of them only, for every range whose end lies
-// inside the set (its waves combined their partials).
+// head, worked side by side; each set with tokens takes set_cost positions, then one per token) is
+// cut into R = min(num_ranges, ceil(T / min_tokens)) ranges; per range it meets, a group owns
+// range_sub consecutive slots from ((set + range) * lanes + lane) * range_sub on -- or
+// (stream_combined) the first of them only, for every range in which the set is the last with
+// tokens (its waves combined their partials).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -48,23 +49,24 @@ __global__ void __launch_bounds__(NT) merge_kernel(MergeArgs a) {
     mbase = (int64_t)row * a.num_parts * 2;
     obase = (int64_t)row * a.num_parts * a.D;
   } else {
-    // stream: tokens of all sequences before b, and of all sequences (each wave sums them itself)
-    long long pre = 0, tot = 0;
-    for (int bb = lane; bb < a.batch; bb += 64) {
-      const long long l = max(0, min(a.lengths[bb], a.len_cap));
-      tot += l;
-      if (bb < b) pre += l;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off /= 2) {
-      pre += __shfl_xor(pre, off, 64);
-      tot += __shfl_xor(tot, off, 64);
-    }
     // sets: L = a.lanes consecutive query groups of one KV head, worked side by side (one
     // workgroup each) on one range
     const int L = a.lanes, QGB = a.qgroups / L, HS = a.HK * QGB;
-    const int64_t T = (int64_t)tot * HS;
-    const int64_t weff = min<int64_t>((int64_t)a.num_ranges, (T + a.min_tokens - 1) / a.min_tokens);
+    // the stream's length, ranges and set cost in force, as the partial kernel computes them;
+    // then the positions of the sequences before b (each wave sums them itself): per set with
+    // tokens, C and then its tokens
+    const StreamSpan sp = stream_span(a.lengths, a.batch, a.len_cap, HS, a.num_ranges, a.min_tokens,
+                                      a.set_cost, lane);
+    const int C = sp.C;
+    long long pre = 0;
+    for (int bb = lane; bb < b; bb += 64) {
+      const long long l = max(0, min(a.lengths[bb], a.len_cap));
+      pre += l > 0 ? l + C : 0;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off /= 2) pre += __shfl_xor(pre, off, 64);
+    const int64_t T = sp.T;
+    const int64_t weff = sp.R;
     const int REP = a.HQ / a.HK;
     const int hk = h / REP;
     const int jj = (h - hk * REP) * a.N + i;
@@ -74,15 +76,17 @@ __global__ void __launch_bounds__(NT) merge_kernel(MergeArgs a) {
     rstride = (int64_t)L * a.range_sub;                          // slots between a lane's ranges
     const int64_t u = (int64_t)b * HS + sq;
     if (len > 0 && weff > 0) {
-      const int64_t start = (int64_t)pre * HS + (int64_t)sq * len;
-      const int64_t end = start + len;
-      const int64_t w_first = start * weff / T, w_last = (end - 1) * weff / T;
+      // the set's tokens sit at positions [first, end), after its C positions
+      const int64_t first = (int64_t)pre * HS + (int64_t)sq * (len + C) + C;
+      const int64_t end = first + len;
+      const int64_t w_first = first * weff / T, w_last = (end - 1) * weff / T;
       if (a.stream_combined) {
-        // a range whose end lies inside the set combined each lane's partials into one (every
-        // range before the last; the last too if it ends where the set ends)
+        // a range in which the set is the last with tokens combined each lane's partials into one:
+        // every range before the last, and the last too unless the next set's first token (C
+        // positions after end) lies inside it
         const int64_t x1_last = ((w_last + 1) * T + weff - 1) / weff;
         nr = (int)(w_last - w_first);
-        nparts = nr + (x1_last == end ? 1 : a.range_sub);
+        nparts = nr + (x1_last <= end + C ? 1 : a.range_sub);
       } else {
         nparts = (int)(w_last - w_first + 1) * a.range_sub;
       }

@@ -893,10 +893,10 @@ partial_part_kernel(PartialArgs a) {
 
 // ------------------------------------------------------------------- balanced stream
 
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+__device__ __forceinline__ long long wave_incl_scan(long long x, int lane) {
 #pragma unroll
   for (int off = 1; off < 64; off *= 2) {
-    const int y = __shfl_up(x, off, 64);
+    const long long y = __shfl_up(x, off, 64);
     if (lane >= off) x += y;
   }
   return x;
@@ -927,34 +927,30 @@ partial_stream_kernel(PartialArgs a) {
   ln = uni(ln);
   const int QGB = a.qgroups / L, HS = a.HK * QGB;                // sets per KV head, per sequence
 
-  // total stream length T (set positions) and the number of working ranges (every wave computes
-  // the same)
-  int64_t tot = 0;
-  for (int c = 0; c < B; c += 64) {
-    const int bb = c + lane;
-    long long s = bb < B ? clamp_len(a, bb) : 0;
-#pragma unroll
-    for (int off = 32; off >= 1; off /= 2) s += __shfl_xor(s, off, 64);
-    tot += s;
-  }
-  const int64_t T = uni64(tot) * HS;
-  const int R = (int)min<int64_t>((int64_t)a.num_ranges, (T + a.min_tokens - 1) / a.min_tokens);
+  // The stream: every set that has tokens takes C positions (the set cost: what changing sets costs
+  // a wave -- its partial written, the next set's q copy and first rows fetched -- counted in
+  // tokens) followed by one position per token; sequences of length 0 take none.  Ranges cut the
+  // stream into equal parts, so a range whose tokens span two sets holds C fewer tokens.
+  // Total length T and the number of working ranges (every wave computes the same):
+  const StreamSpan sp = stream_span(a.lengths, B, a.len_cap, HS, a.num_ranges, a.min_tokens, a.set_cost, lane);
+  const int C = sp.C;
+  const int64_t T = sp.T;
+  const int R = sp.R;
   if (g >= R) return;                                            // whole workgroup
   const int64_t x0 = ((int64_t)g * T + R - 1) / R;
   const int64_t x1 = ((int64_t)(g + 1) * T + R - 1) / R;
   if (x0 >= x1) return;                                          // whole workgroup
-  if (threadIdx.x == 0) tile_ctr = 0;
-  __syncthreads();
 
   // locate the sequence holding stream position x0 (the first with prefix end > x0)
   int b = -1;
-  int64_t pb = 0;                                                // tokens of sequences before b
+  int64_t pb = 0;                                                // positions of sequences before b
   {
     int64_t base = 0;
     for (int c = 0; c < B; c += 64) {
       const int bb = c + lane;
-      const int lv = bb < B ? clamp_len(a, bb) : 0;
-      const int incl = wave_incl_scan(lv, lane);
+      const int l = bb < B ? clamp_len(a, bb) : 0;
+      const long long lv = l > 0 ? (long long)l + C : 0;
+      const long long incl = wave_incl_scan(lv, lane);
       const uint64_t hit = __ballot((base + incl) * HS > x0 && lv > 0);
       if (hit) {
         const int k = __builtin_ctzll(hit);
@@ -962,14 +958,20 @@ partial_stream_kernel(PartialArgs a) {
         pb = uni64(base + __shfl(incl, k, 64) - __shfl(lv, k, 64));
         break;
       }
-      base += uni(__shfl(incl, 63, 64));
+      base += uni64(__shfl(incl, 63, 64));
     }
   }
   if (b < 0) return;                                             // x0 < T: not reached
   int len = uni(clamp_len(a, b));
-  const int64_t rem = x0 - pb * HS;
-  int uu = uni((int)(rem / len));                                // set within the sequence
-  int t_lo = uni((int)(rem - (int64_t)uu * len));
+  int64_t lp = (int64_t)len + C;                                 // positions of one set of b
+  int uu = uni((int)((x0 - pb * HS) / lp));                      // set within the sequence
+  int64_t start = pb * HS + (int64_t)uu * lp;                    // the set's first position
+  // the range's tokens of this set: [t_lo, t_hi); none if the range lies within its C positions
+  int t_lo = uni((int)max<int64_t>(0, x0 - start - C));
+  int t_hi = uni((int)min<int64_t>(len, x1 - start - C));
+  if (t_hi <= t_lo) return;                                      // whole workgroup
+  if (threadIdx.x == 0) tile_ctr = 0;
+  __syncthreads();
 
   // The range is a list of tiles: set by set, the set's part of the range cut into 64-token
   // tiles.  The workgroup's waves take tiles from one LDS counter, so faster waves take more of
@@ -987,10 +989,9 @@ partial_stream_kernel(PartialArgs a) {
   int kbase = 0;                                                 // first tile of the current set
   float* const opart = a.opart;
   float* const ml = a.ml;
-  int64_t x = x0;
-  while (x < x1) {
-    const int seg = (int)min<int64_t>((int64_t)(len - t_lo), x1 - x);
-    const int t_end = t_lo + seg, ntiles = (seg + PV_TILE - 1) / PV_TILE;
+  while (true) {
+    const int seg = t_hi - t_lo;                                 // > 0
+    const int t_end = t_hi, ntiles = (seg + PV_TILE - 1) / PV_TILE;
     Unit un;
     un.b = b; un.hk = uu / QGB; un.qg = (uu - un.hk * QGB) * L + ln; un.len = len;
     un.u = ((int64_t)b * a.HK + un.hk) * a.qgroups + un.qg;
@@ -1008,7 +1009,11 @@ partial_stream_kernel(PartialArgs a) {
         ws[wave], st, lane);
     kq = uni(kq);
     const int64_t slot = (((int64_t)b * HS + uu + g) * L + ln) * NW;
-    if (x + seg < x1) {
+    // the next set starts at position start + lp; it has a token in the range if its first token,
+    // C positions on, comes before x1 (a later set then too, and the next one has tokens: empty
+    // sequences take no positions)
+    const int64_t next = start + lp;
+    if (next + C < x1) {
       // a set that ends inside the range: one partial per wave (no barrier: the waves that are
       // done with its tiles go on to the next set)
       acc_write<BITS, DV, QVW, GS>(
@@ -1017,17 +1022,16 @@ partial_stream_kernel(PartialArgs a) {
             ml[((slot + wave) * QVW + j) * 2] = m; ml[((slot + wave) * QVW + j) * 2 + 1] = l;
           });
       kbase += ntiles;
-      x += seg;
-      t_lo += seg;
-      if (t_lo >= len) {
-        t_lo = 0;
-        if (++uu == HS) {
-          uu = 0;
-          do { ++b; } while (b < B && clamp_len(a, b) == 0);
-          if (b >= B) break;                                     // (x1 <= T: not reached)
-          len = uni(clamp_len(a, b));
-        }
+      if (++uu == HS) {
+        uu = 0;
+        do { ++b; } while (b < B && clamp_len(a, b) == 0);
+        if (b >= B) break;                                       // (next < T: not reached)
+        len = uni(clamp_len(a, b));
+        lp = (int64_t)len + C;
       }
+      start = next;
+      t_lo = 0;
+      t_hi = uni((int)min<int64_t>(len, x1 - start - C));        // >= 1
       continue;
     }
     // the range's last set: each wave, done with its tiles, puts its partial in its own scratch;

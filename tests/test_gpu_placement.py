@@ -5,7 +5,7 @@ a second pool with more blocks (the extra ones never written) whose block table 
 logical block to another physical block through a seeded permutation.  The kernels meet tokens
 in logical order and only their load addresses differ, so fixed partitions and the matrix
 engine (both repeat bit for bit) give bit-identical outputs, and the balanced stream agrees to
-f32 rounding.  The pools' rows, read back through kv_gather_debug, are identical as well."""
+f32 rounding (its waves take tiles as they come free, so the order of its sums varies).  The pools' rows, read back through kv_gather_debug, are identical as well."""
 import numpy as np
 import pytest
 import torch
@@ -52,7 +52,10 @@ def test_block_placement_does_not_change_output(name, bits, BS):
         assert np.array_equal(a, b)
         a = G.run_decode(w, pa, partition_tokens=kvq.PARTITION_STREAM)
         b = G.run_decode(w, pb, partition_tokens=kvq.PARTITION_STREAM, table=t2)
-        assert np.abs(a - b).max() <= 1e-6 * np.abs(a).max()
+        # the stream's waves take tiles as they come free, so the two runs sum in different orders
+        # and rescale at different points: f32 rounding of sums over up to max_len tokens, a few
+        # ulps per sqrt(token)
+        assert np.abs(a - b).max() <= 4 * 2.0 ** -24 * np.sqrt(w.max_len) * np.abs(a).max()
         if bits == 4 and w.group == 64 and w.D in (128, 256):
             a = G.run_decode(w, pa, engine=kvq.ENGINE_MATRIX)
             b = G.run_decode(w, pb, engine=kvq.ENGINE_MATRIX, table=t2)
