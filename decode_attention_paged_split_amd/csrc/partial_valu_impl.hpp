@@ -390,7 +390,6 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
                         KPB <= KPBV && KCP >= 4 && 64 % KCP == 0 && 64 % KCPV == 0;
   int tt = uni(grab());
   if (tt >= t1) return;
-  int tn_raw = grab();
 
   const int vsl = lane % VLPR, vrg = lane / VLPR;                // V: dim slot, row in read
   const int N = a.N;
@@ -486,11 +485,13 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
   else vcur = load_row_part<KCPV>(vplane, row, ROWBV, 0);
 
   while (true) {
-    const int tn = uni(tn_raw);
+    // the next tile is claimed only as this one starts, so that a wave holds no more than the
+    // tile it works and the one it prefetches: near the end of a range the last tiles go to the
+    // waves that are free
+    const int tn = uni(grab());
     const bool has_next = tn < t1;                                // uniform
     const int t_next = min(tn + lane, t1 - 1);
     const int tbl_next = has_next ? table_entry(t_next) : 0;
-    const int tnn_raw = has_next ? grab() : t1;                   // the tile after next
 
     // ---- K phase: z[j] = q_j . k_t for this lane's token.
     // q block b = ((g * NHB + hb) * QVW + j): the 16 q pairs of 16-pair block hb of scale group g
@@ -682,7 +683,6 @@ __device__ __forceinline__ void run_tiles(const PartialArgs& a, const Unit& un, 
 
     if (!has_next) break;
     tt = tn;
-    tn_raw = tnn_raw;
     row = row_next;
     sc = scn;
   }
@@ -983,9 +983,9 @@ partial_stream_kernel(PartialArgs a) {
   auto take = [&]() {
     int k = 0;
     if (lane == 0) k = atomicAdd(&tile_ctr, 1);
-    return k;                                                    // valid in lane 0
+    return uni(k);
   };
-  int kq = uni(take());                                          // next tile this wave takes
+  int kq = -1;                          // a tile this wave claimed for a later set (-1: none)
   int kbase = 0;                                                 // first tile of the current set
   float* const opart = a.opart;
   float* const ml = a.ml;
@@ -1001,13 +1001,14 @@ partial_stream_kernel(PartialArgs a) {
     run_tiles<BITS, D, DV, QVW, GS>(
         a, un, t_end,
         [&]() {
-          const int k = uni(kq);
+          // claim a tile as it is needed; one that lies in a later set is kept for it
+          if (kq < 0) kq = take();
+          const int k = kq;
           if (k - kb >= ntiles) return t_end;                    // the set's tiles are all taken
-          kq = take();
+          kq = -1;
           return t0u + (k - kb) * PV_TILE;
         },
         ws[wave], st, lane);
-    kq = uni(kq);
     const int64_t slot = (((int64_t)b * HS + uu + g) * L + ln) * NW;
     // the next set starts at position start + lp; it has a token in the range if its first token,
     // C positions on, comes before x1 (a later set then too, and the next one has tokens: empty
