@@ -909,8 +909,8 @@ partial_stream_kernel(PartialArgs a) {
   // the waves' tile scratch; a wave done with the range's last set puts its partial of it in its
   // own scratch for the combine: [QVW][DV] o, then [QVW] m, then [QVW] l
   __shared__ __align__(16) WaveScratch<BITS, DV, QVW, GS> ws[NW];
-  static_assert(sizeof(WaveScratch<BITS, DV, QVW, GS>) >= (QVW * DV + 2 * QVW) * sizeof(float),
-                "a wave's partial fits its scratch");
+  static_assert(sizeof(WaveScratch<BITS, DV, QVW, GS>) >= (QVW * DV + 2 * QVW + NW * QVW) * sizeof(float),
+                "a wave's partial, and after wave 0's the combine's factor table, fit its scratch");
   __shared__ int tile_ctr;                                       // next tile of the range
 
   const int lane = threadIdx.x & 63;
@@ -1045,25 +1045,34 @@ partial_stream_kernel(PartialArgs a) {
           [&](int j, float m, float l) { mine[QVW * DV + j] = m; mine[QVW * DV + QVW + j] = l; });
     }
     __syncthreads();
+    // one lane per vector: the running max M over the waves, each wave's factor 2^(m_w - M) (0 for
+    // a wave that saw no token) and the combined normaliser, into a table after wave 0's partial;
+    // then every thread of the workgroup sums the waves' o for its elements with those factors
     auto part = [&](int w) { return reinterpret_cast<const float*>(&ws[w]); };
-    for (int e = threadIdx.x; e < QVW * DV; e += NW * 64) {
-      const int j = e / DV, d = e - j * DV;
+    float* tab = reinterpret_cast<float*>(&ws[0]) + QVW * DV + 2 * QVW;   // [NW][QVW] factors
+    if (threadIdx.x < QVW) {
+      const int j = threadIdx.x;
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < NW; ++w) M = fmaxf(M, part(w)[QVW * DV + j]);
-      float num = 0.0f, den = 0.0f;
-      if (M != -INFINITY) {
+      float den = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          const float mw = part(w)[QVW * DV + j];
-          if (mw == -INFINITY) continue;
-          const float f = fast_exp2(mw - M);
-          num = fmaf(f, part(w)[j * DV + d], num);
-          den = fmaf(f, part(w)[QVW * DV + QVW + j], den);
-        }
+      for (int w = 0; w < NW; ++w) {
+        const float mw = part(w)[QVW * DV + j];
+        const float f = (M == -INFINITY || mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
+        tab[w * QVW + j] = f;
+        den = fmaf(f, part(w)[QVW * DV + QVW + j], den);
       }
+      ml[(slot * QVW + j) * 2] = M;
+      ml[(slot * QVW + j) * 2 + 1] = den;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < QVW * DV; e += NW * 64) {
+      const int j = e / DV, d = e - j * DV;
+      float num = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) num = fmaf(tab[w * QVW + j], part(w)[j * DV + d], num);
       opart[(slot * QVW + j) * DV + d] = num;
-      if (d == 0) { ml[(slot * QVW + j) * 2] = M; ml[(slot * QVW + j) * 2 + 1] = den; }
     }
     break;
   }
