@@ -103,10 +103,6 @@ __device__ __forceinline__ float block_reduce(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Range w and lane ln of workgroup i of nwg on the balanced stream when the L query groups of a set
-// (one KV head's L consecutive groups) run side by side, one workgroup each, over the same range:
-// workgroups are handed to the 8 XCDs (each with its own L2) in turn by index, so the L workgroups
-// of a range are taken 8 indices apart (one XCD) and an XCD's ranges are consecutive.  L = 1: w = i.
 // Stream schedule: its length T in positions, the number R of working ranges and the set cost C in
 // force.  A set (a KV head's query groups worked together) of a sequence with tokens takes C
 // positions and then one per token.  C is the requested cost unless every range would hold the
@@ -152,6 +148,10 @@ __device__ __forceinline__ StreamSpan stream_span(const int32_t* lengths, int B,
   return r;
 }
 
+// Range w and lane ln of workgroup i of nwg on the balanced stream when the L query groups of a set
+// (one KV head's L consecutive groups) run side by side, one workgroup each, over the same range:
+// workgroups are handed to the 8 XCDs (each with its own L2) in turn by index, so the L workgroups
+// of a range are taken 8 indices apart (one XCD) and an XCD's ranges are consecutive.  L = 1: w = i.
 __device__ __forceinline__ void stream_range_lane(int L, int i, int nwg, int& w, int& ln) {
   if (L > 1 && nwg % (8 * L) == 0) {
     const int q = i >> 3;
