@@ -132,8 +132,11 @@ __device__ __forceinline__ StreamSpan stream_span(const int32_t* lengths, int B,
     }
     tok += s; nz += n; lmin = min(lmin, mn); lmax = max(lmax, mx);
   }
-  tok = __builtin_amdgcn_readfirstlane((int)(tok & 0xffffffff)) |
-        ((long long)__builtin_amdgcn_readfirstlane((int)(tok >> 32)) << 32);
+  {                                     // every lane holds the sums; take them as scalars
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)tok);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)tok >> 32));
+    tok = (long long)(((uint64_t)hi << 32) | lo);
+  }
   nz = __builtin_amdgcn_readfirstlane((int)nz);
   lmin = __builtin_amdgcn_readfirstlane(lmin);
   lmax = __builtin_amdgcn_readfirstlane(lmax);

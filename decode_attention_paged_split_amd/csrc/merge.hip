@@ -77,7 +77,7 @@ __global__ void __launch_bounds__(NT) merge_kernel(MergeArgs a) {
     const int64_t u = (int64_t)b * HS + sq;
     if (len > 0 && weff > 0) {
       // the set's tokens sit at positions [first, end), after its C positions
-      const int64_t first = (int64_t)pre * HS + (int64_t)sq * (len + C) + C;
+      const int64_t first = (int64_t)pre * HS + (int64_t)sq * ((int64_t)len + C) + C;
       const int64_t end = first + len;
       const int64_t w_first = first * weff / T, w_last = (end - 1) * weff / T;
       if (a.stream_combined) {
