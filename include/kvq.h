@@ -16,6 +16,12 @@
  *                           partition_tokens == 0 by fixed partitions of n tokens.
  *   KVQ_MFMA_RANGES_PER_CU=n  ranges per compute unit of the matrix-core engine's stream
  *                           (2..16; default 4 at head dim 256, 8 at 128).
+ *   KVQ_STREAM_LANES=n      query groups of a KV head worked side by side on the balanced
+ *                           stream (1, 2 or 4, dividing the group count; default 4, 2 or 1 by
+ *                           divisibility).
+ *   KVQ_SET_COST=n          vector engine, balanced stream: positions charged per (sequence, KV
+ *                           head) set ahead of its tokens, so that ranges that change sets get
+ *                           fewer tokens (0..4096; default 512).
  *
  * Conventions shared by every entry point
  *   - Return value: KVQ_OK (0) or a negative kvq_status.  A failing call enqueues
