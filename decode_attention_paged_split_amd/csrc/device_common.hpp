@@ -79,6 +79,54 @@ __device__ __forceinline__ float xstep(float x) {
   }
 }
 
+// Integer forms over all 64 lanes, for the stream's lengths: an all-reduce (every lane ends with
+// the result) and an inclusive prefix sum (row shifts 1, 2, 4, 8 within each row of 16, then the
+// row broadcasts of lanes 15 and 31), both on DPP and the permlane swaps.  Sums of values below
+// 2^32 go through two 32-bit halves (16 bits and the rest), each summing exactly over 64 lanes.
+struct OpAddU { __device__ static uint32_t f(uint32_t a, uint32_t b) { return a + b; } };
+struct OpMinU { __device__ static uint32_t f(uint32_t a, uint32_t b) { return a < b ? a : b; } };
+struct OpMaxU { __device__ static uint32_t f(uint32_t a, uint32_t b) { return a > b ? a : b; } };
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+template <class OP>
+__device__ __forceinline__ uint32_t wave_all_u32(uint32_t x) {
+  x = OP::f(x, dpp_u32<DPP_QUAD_1032>(x));
+  x = OP::f(x, dpp_u32<DPP_QUAD_2301>(x));
+  x = OP::f(x, dpp_u32<DPP_ROW_HALF_MIRROR>(x));
+  x = OP::f(x, dpp_u32<DPP_ROW_MIRROR>(x));
+  {
+    auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = OP::f(r[0], r[1]);
+  }
+  auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return OP::f(r[0], r[1]);
+}
+__device__ __forceinline__ uint64_t wave_sum_u64(uint32_t x) {
+  const uint32_t lo = wave_all_u32<OpAddU>(x & 0xFFFFu), hi = wave_all_u32<OpAddU>(x >> 16);
+  return ((uint64_t)hi << 16) + lo;
+}
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+__device__ __forceinline__ uint64_t wave_scan_u64(uint32_t x) {
+  const uint32_t lo = wave_scan_u32(x & 0xFFFFu), hi = wave_scan_u32(x >> 16);
+  return ((uint64_t)hi << 16) + lo;
+}
+// lane k's value of a 64-bit x, k uniform
+__device__ __forceinline__ uint64_t lane_u64(uint64_t x, int k) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, k);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), k);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // All-reduce over the 8 lanes i, i ^ 8, i ^ 16, ..., i ^ 56 (every lane's value may differ):
 // exact xor steps at distances 8, 16 and 32.
 template <class OP>
@@ -116,31 +164,25 @@ struct StreamSpan {
 };
 __device__ __forceinline__ StreamSpan stream_span(const int32_t* lengths, int B, int len_cap, int HS,
                                                   int num_ranges, int min_tokens, int set_cost, int lane) {
-  long long tok = 0, nz = 0;
-  int lmin = 0x7fffffff, lmax = 0;
+  uint64_t tok = 0;
+  uint32_t nz = 0, lmin = 0x7fffffffu, lmax = 0;
   for (int c = 0; c < B; c += 64) {
     const int bb = c + lane;
-    const int l = bb < B ? max(0, min(lengths[bb], len_cap)) : 0;
-    long long s = l, n = l > 0 ? 1 : 0;
-    int mn = l > 0 ? l : 0x7fffffff, mx = l;
-#pragma unroll
-    for (int off = 32; off >= 1; off /= 2) {
-      s += __shfl_xor(s, off, 64);
-      n += __shfl_xor(n, off, 64);
-      mn = min(mn, __shfl_xor(mn, off, 64));
-      mx = max(mx, __shfl_xor(mx, off, 64));
-    }
-    tok += s; nz += n; lmin = min(lmin, mn); lmax = max(lmax, mx);
+    const uint32_t l = bb < B ? (uint32_t)max(0, min(lengths[bb], len_cap)) : 0u;
+    tok += wave_sum_u64(l);
+    nz += wave_all_u32<OpAddU>(l > 0 ? 1u : 0u);
+    lmin = min(lmin, wave_all_u32<OpMinU>(l > 0 ? l : 0x7fffffffu));
+    lmax = max(lmax, wave_all_u32<OpMaxU>(l));
   }
-  {                                     // every lane holds the sums; take them as scalars
+  {                                     // every lane holds the results; take them as scalars
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)tok);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)tok >> 32));
-    tok = (long long)(((uint64_t)hi << 32) | lo);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(tok >> 32));
+    tok = ((uint64_t)hi << 32) | lo;
   }
-  nz = __builtin_amdgcn_readfirstlane((int)nz);
-  lmin = __builtin_amdgcn_readfirstlane(lmin);
-  lmax = __builtin_amdgcn_readfirstlane(lmax);
-  const int64_t T0 = tok * HS, S = nz * HS;
+  nz = (uint32_t)__builtin_amdgcn_readfirstlane((int)nz);
+  lmin = (uint32_t)__builtin_amdgcn_readfirstlane((int)lmin);
+  lmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)lmax);
+  const int64_t T0 = (int64_t)tok * HS, S = (int64_t)nz * HS;
   const int R0 = (int)min<int64_t>((int64_t)num_ranges, (T0 + min_tokens - 1) / min_tokens);
   int C = set_cost;
   if (S > 0 && R0 > 0 && lmin == lmax && (R0 % S == 0 || S % R0 == 0)) C = 0;

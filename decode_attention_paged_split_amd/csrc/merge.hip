@@ -59,12 +59,11 @@ __global__ void __launch_bounds__(NT) merge_kernel(MergeArgs a) {
                                       a.set_cost, lane);
     const int C = sp.C;
     long long pre = 0;
-    for (int bb = lane; bb < b; bb += 64) {
-      const long long l = max(0, min(a.lengths[bb], a.len_cap));
-      pre += l > 0 ? l + C : 0;
+    for (int c = 0; c < b; c += 64) {
+      const int bb = c + lane;
+      const int l = bb < b ? max(0, min(a.lengths[bb], a.len_cap)) : 0;
+      pre += (long long)wave_sum_u64(l > 0 ? (uint32_t)l + (uint32_t)C : 0u);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off /= 2) pre += __shfl_xor(pre, off, 64);
     const int64_t T = sp.T;
     const int64_t weff = sp.R;
     const int REP = a.HQ / a.HK;

@@ -893,14 +893,6 @@ partial_part_kernel(PartialArgs a) {
 
 // ------------------------------------------------------------------- balanced stream
 
-__device__ __forceinline__ long long wave_incl_scan(long long x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off *= 2) {
-    const long long y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
 
 template <int BITS, int D, int DV, int QVW, int GS>
 __global__ void __launch_bounds__(VALU_STREAM_WAVES * 64, 1)
@@ -949,16 +941,16 @@ partial_stream_kernel(PartialArgs a) {
     for (int c = 0; c < B; c += 64) {
       const int bb = c + lane;
       const int l = bb < B ? clamp_len(a, bb) : 0;
-      const long long lv = l > 0 ? (long long)l + C : 0;
-      const long long incl = wave_incl_scan(lv, lane);
+      const uint32_t lv = l > 0 ? (uint32_t)l + (uint32_t)C : 0u;   // < 2^31 + 4097
+      const int64_t incl = (int64_t)wave_scan_u64(lv);
       const uint64_t hit = __ballot((base + incl) * HS > x0 && lv > 0);
       if (hit) {
         const int k = __builtin_ctzll(hit);
         b = uni(c + k);
-        pb = uni64(base + __shfl(incl, k, 64) - __shfl(lv, k, 64));
+        pb = base + (int64_t)lane_u64((uint64_t)incl, k) - (int64_t)lane_u64(lv, k);
         break;
       }
-      base += uni64(__shfl(incl, 63, 64));
+      base += (int64_t)lane_u64((uint64_t)incl, 63);
     }
   }
   if (b < 0) return;                                             // x0 < T: not reached
