@@ -16,7 +16,10 @@
 //
 // gfx950 layout (not the pages' Metal one).  A unit is (sequence, KV head, query group of QVW
 // vectors); a wave walks tiles of 64 consecutive tokens of a unit.  Per tile:
-//  1. K phase, one token per lane.  The lane loads its token's row with 16-byte loads, turns
+//  1. K phase, one token per lane.  The tile's rows arrive with 16-byte loads (rows of 64 to 128
+//     bytes, and affine rows of two 128-byte parts at scale groups of 64 or more, coalesced:
+//     consecutive lanes read consecutive pieces in token order, and each piece reaches its
+//     token's lane through LDS; other rows one token per lane).  The lane turns its token's
 //     codes into bf16 pairs (4/2-bit codes c as bf16(128 + c) with one v_and_or, 8-bit codes
 //     through an exact f32 conversion, bf16 rows as they are) and meets q in v_dot2_f32_bf16
 //     with the q pair in a scalar register: q sits in the workspace in the codes' pair order
@@ -29,8 +32,8 @@
 //     max and the rescale of o, l and the bias sums run only then), so p = 2^(z - m) <= 2^8.
 //     Each lane keeps its share of the normaliser l and of the bias sum sum_t p b_v per scale
 //     group; the weights p * s_v (per vector and scale group) go to LDS.
-//  3. V phase.  The lane loads its token's V row like the K row (16-byte loads, same address
-//     arithmetic), writes it to LDS, and the tile is read back transposed: VLPR lanes per row,
+//  3. V phase.  The tile's V rows are loaded like its K rows and staged in LDS, and the tile is
+//     read back transposed: VLPR lanes per row,
 //     each owning VDPL head dims.  Codes become f32 with v_cvt_f32_ubyteN and accumulate as
 //     o[vector][dim] += (p s)[vector] * code in f32.
 // At the end of a wave's range the lanes' shares are summed and o += sum_t p b_v, so the
@@ -45,14 +48,15 @@
 //    sequence); its 4 waves interleave tiles and combine in LDS; one partial per partition.
 //  * balanced stream (partition_tokens == 0): a set is L consecutive query groups of one KV
 //    head of one sequence (L = 4 when a KV head's groups come in fours, 2 in pairs, else 1).
-//    Every cached token of every set is laid end to end in one stream of T positions, cut into
-//    R equal ranges (R = min(compute units / L, ceil(T / 512))); each range is worked by L
+//    Every set with tokens is laid end to end in one stream, taking a set cost of C positions (a
+//    wave's change of set, in tokens) and then one per token, T positions in all, cut into R
+//    equal ranges (R = min(compute units / L, ceil(T / 512))); each range is worked by L
 //    workgroups of 8 waves, one per group of the set (one workgroup per compute unit), placed on
 //    one XCD so that the K/V rows one of them fetches are found in that XCD's L2 by the others,
 //    which walk the same tiles at about the same pace.  A workgroup's waves share its range's
-//    64-token tiles through an LDS counter: the two waves on a SIMD do not progress at the same
-//    rate (the older one has issue priority), and a static split would leave the slower one
-//    running alone at the end.  Each wave writes one partial per set that ends inside its range,
+//    64-token tiles through an LDS counter, each claiming its next tile as the current one
+//    starts: the two waves on a SIMD do not progress at the same rate (the older one has issue
+//    priority), and a static split would leave the slower one running alone at the end.  Each wave writes one partial per set that ends inside its range,
 //    at slot ((set + r) * L + lane) * 8 + wave (distinct for every (set, range, lane, wave)
 //    because ranges are contiguous and ordered); for the range's last set the 8 waves' partials
 //    are combined in LDS first and written once, at slot ((set + r) * L + lane) * 8.  (A combine
@@ -892,7 +896,6 @@ partial_part_kernel(PartialArgs a) {
 }
 
 // ------------------------------------------------------------------- balanced stream
-
 
 template <int BITS, int D, int DV, int QVW, int GS>
 __global__ void __launch_bounds__(VALU_STREAM_WAVES * 64, 1)
