@@ -7,7 +7,9 @@ merge must place and find the partials alike at any C.  Checked against the orac
 abs and rel L2 2e-3), with the cost forced through KVQ_SET_COST:
 - ragged 4-bit GQA-8 sequences with one empty sequence, C = 0, 512 (the default) and 4096 (more
   than a range: some ranges hold only charged positions and write nothing);
-- four query groups side by side (4 rows x GQA 8, 32 vectors per KV head), C = 0 and 4096;
+- four query groups side by side (4 rows x GQA 8, 32 vectors per KV head), C = 0 and 4096, and
+  with 130 short sequences (three of them empty: the stream's prefix sums cross 64-lane chunks),
+  C = 0 and 512;
 - equal lengths, where the cost is dropped, C = 512 and 4096;
 - bf16 pages with ragged lengths, C = 0 and 4096.
 Every output comes from libkvq through the C ABI."""
@@ -60,6 +62,23 @@ def test_groups_side_by_side(cost):
     w = make_workload("c5", B=3, len_lo=300, len_hi=2500)
     ref = attention.workload_output(w)
     err, rl2 = G.check_f32(_run(w, cost), ref, tag=f"c5 set cost {cost}")
+    print(f"  max abs {err:.2e} rel L2 {rl2:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("cost", [0, 512])
+def test_many_sequences_groups_side_by_side(cost):
+    # 130 short sequences (the stream's prefix sums cross two 64-lane chunks), four query groups
+    # side by side, a few sequences empty
+    print(f"130 sequences, 4 groups side by side, set cost {cost}", flush=True)
+    w = make_workload("c5", B=130, len_lo=40, len_hi=400, N=4, HQ=8, HK=1)
+    ref = attention.workload_output(w)
+    lengths = w.lengths.astype(np.int32).copy()
+    empty = [0, 64, 127]
+    lengths[empty] = 0
+    got = _run(w, cost, lengths)
+    keep = [b for b in range(w.B) if b not in empty]
+    err, rl2 = G.check_f32(got[keep], ref[keep], tag=f"130 sequences, set cost {cost}")
+    assert np.all(got[empty] == 0.0)
     print(f"  max abs {err:.2e} rel L2 {rl2:.2e}", flush=True)
 
 
