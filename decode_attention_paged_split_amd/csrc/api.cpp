@@ -571,7 +571,11 @@ struct Plan {
 // four partials each; many rows keep every compute unit busy anyway, and then streams of about
 // eight partials waste fewer waves on the row's set-up (measured: 512 rows of 17-40 partials run
 // fastest at 4-10 per stream, 8192 rows of 3-10 partials at one stream).  Partials per row: the
-// fixed partitions' count, or the stream slots of a unit spread over its rows.
+// fixed partitions' count, or the stream's slots for a unit, sub in every range it meets (each of
+// its rows reads them all).  The vector engine's stream combines a unit's slots in all but the
+// last range it meets, so its rows read fewer than this counts (the 4-bit GQA-8 decode at 32
+// sequences: 2-15, against 40 counted); the sizes it gives measured best there as well (256
+// threads: 9.4 us against 9.8 at 128 and 10.5 at 64).
 int merge_threads_for(int dv, int pt, int parts, const StreamGeom& sg, double units, double rows) {
   const double per_row = pt > 0 ? (double)parts : (double)sg.sub * (sg.ranges + units) / units;
   const double per_stream = rows >= 8.0 * device_cus() ? 8.0 : 4.0;
