@@ -22,6 +22,8 @@
  *   KVQ_SET_COST=n          vector engine, balanced stream: positions charged per (sequence, KV
  *                           head) set ahead of its tokens, so that ranges that change sets get
  *                           fewer tokens (0..4096; default 512).
+ * Each call reads these when it is made; they decide where the partials lie, so a partial call
+ * and the merge call that reads its partials must run under the same values.
  *
  * Conventions shared by every entry point
  *   - Return value: KVQ_OK (0) or a negative kvq_status.  A failing call enqueues
